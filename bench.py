@@ -1,0 +1,269 @@
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+One step = one full layer call (router, top-k, permutation and offsets,
+grouped w13+SwiGLU GEMM, grouped down GEMM, finalize) over the denoise layer
+(T=4096 image tokens, hidden 4096, 64 experts, top-8, TP2-shard intermediate
+1536 per expert, bf16), inputs resident in HBM.  Prints ONE JSON line with the
+layer throughput (TFLOP/s of expert math, tokens/s), the dominant kernel's
+roofline position measured with HIP events, the other workload layers
+(2-micro denoise, AR decode in GB/s, skewed CFG batch) and the CPU oracle's
+rate on a bounded sample of the same layer.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import moe_inputs as mi  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE layer TFLOP/s + tokens/s (T=4096, 64E top-8 bf16); decode GB/s; % roofline"
+
+
+def expert_flops(sp) -> float:
+    """Algorithmic expert FLOPs of one call: 2*T*k*H*(2I) for gate|up plus
+    2*T*k*I*H for down."""
+    return 6.0 * sp.T * sp.k * sp.H * sp.I
+
+
+def w13_flops(sp) -> float:
+    return 4.0 * sp.T * sp.k * sp.H * sp.I
+
+
+def decode_bytes(sp, n_active: int) -> int:
+    """Algorithmic HBM bytes of a decode call: the active experts' w13 and
+    down weights once, x and out once, the router weights once."""
+    per_expert = (2 * sp.I * sp.H + sp.H * sp.I) * 2
+    return n_active * per_expert + sp.T * sp.H * 2 * 2 + sp.E * sp.H * 4
+
+
+def dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def upload(inp, torch):
+    return dict(x=dev(inp.x, torch), wg=dev(inp.wg, torch),
+                bias=None if inp.bias is None else dev(inp.bias, torch),
+                w1=dev(inp.w1, torch), w2=dev(inp.w2, torch), sp=inp.spec)
+
+
+def relayout_two_micro(base, sp):
+    """The 1-micro layer's weights stored micro-major as 2 micros."""
+    I, Im = base.spec.I, sp.Im
+    w1 = np.empty((2, sp.E, 2 * Im, sp.H), np.uint16)
+    w2 = np.empty((2, sp.E, sp.H, Im), np.uint16)
+    for m in range(2):
+        w1[m, :, :Im] = base.w1[0, :, m * Im:(m + 1) * Im]
+        w1[m, :, Im:] = base.w1[0, :, I + m * Im:I + (m + 1) * Im]
+        w2[m] = base.w2[0, :, :, m * Im:(m + 1) * Im]
+    return w1, w2
+
+
+def time_forward(moe, torch, d, steps, warmup):
+    """Median-free plain average over exactly `steps` timed calls of
+    moe_forward, bracketed by device synchronisation."""
+    sp = d["sp"]
+    shape = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
+    buf = moe.MoELayerBuffers(shape)
+    for _ in range(warmup):
+        buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev_ms = e0.elapsed_time(e1) / steps
+    return ev_ms, wall_ms, buf
+
+
+def time_kernels(moe, torch, d, steps, warmup):
+    """Per-kernel average durations (ms): the same five kernels through the
+    step-wise entry points, each bracketed by HIP events on the launch
+    stream (torch's current stream)."""
+    sp = d["sp"]
+    s = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
+    T, E, k, H, R = sp.T, sp.E, sp.k, sp.H, sp.T * sp.k
+    dt = torch.bfloat16 if sp.dtype == mi.BF16 else torch.float32
+    f = lambda *shape, dtype=torch.float32: torch.empty(*shape, dtype=dtype, device="cuda")  # noqa: E731
+    L, ids, w = f(T, E), f(T, k, dtype=torch.int32), f(T, k)
+    cnt, off = f(E, dtype=torch.int32), f(E + 1, dtype=torch.int32)
+    perm, inv = f(R, dtype=torch.int32), f(R, dtype=torch.int32)
+    h, y, out = f(R, sp.I, dtype=dt), f(R, H, dtype=dt), f(T, H, dtype=dt)
+    names = ["route", "permute", "w13_swiglu", "down", "finalize"]
+    calls = [
+        lambda: moe.moe_route(s, d["x"], d["wg"], d["bias"], L, ids, w),
+        lambda: moe.moe_permute(s, ids, cnt, off, perm, inv),
+        lambda: moe.moe_grouped_gemm_w13_swiglu(s, d["x"], perm, off, d["w1"], h),
+        lambda: moe.moe_grouped_gemm_down(s, h, off, d["w2"], y),
+        lambda: moe.moe_finalize(s, y, inv, w, out),
+    ]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in calls] for _ in range(steps)]
+    for i in range(steps):
+        for j, c in enumerate(calls):
+            evs[i][j][0].record()
+            c()
+            evs[i][j][1].record()
+    torch.cuda.synchronize()
+    res = {}
+    for j, n in enumerate(names):
+        res[n] = float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)]))
+    return res, cnt.cpu().numpy()
+
+
+def cpu_baseline(base, n_tokens: int):
+    """The oracle as it stands, on the first n_tokens tokens of the layer."""
+    import dataclasses
+
+    import oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    sp = dataclasses.replace(base.spec, T=n_tokens)
+    inp = mi.LayerInputs(sp, base.x[:n_tokens], base.wg, base.bias, base.w1, base.w2)
+    t0 = time.perf_counter()
+    o.forward(inp)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(expert_flops(sp) / dt / 1e12, 6), "unit": "TFLOP/s",
+        "tokens_per_s": round(n_tokens / dt, 2), "seconds": round(dt, 2), "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle forward (fp64 numpy, full routing + all {sp.E} experts) on the first "
+                  f"{n_tokens} of {base.spec.T} tokens of the same layer",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the decode, 2-micro and skewed layers")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is measured "
+              f"on one GPU's shard, and no multi-GPU path is built.", file=sys.stderr)
+        return 2
+
+    import torch
+    import mixture_experts_ffn_moe_amd as moe
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+
+    sp = mi.spec(1)
+    log(f"generating {sp.name}")
+    base = mi.make_layer(sp)
+    d = upload(base, torch)
+    log("timing moe_forward")
+    ms, wall_ms, buf = time_forward(moe, torch, d, args.steps, args.warmup)
+    log(f"layer {ms:.4f} ms/step (wall {wall_ms:.4f})")
+    kern, counts = time_kernels(moe, torch, d, args.steps, args.warmup)
+    log("kernels " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in kern.items()))
+
+    flops = expert_flops(sp)
+    value = flops / (ms * 1e-3) / 1e12
+    w13_ms = kern["w13_swiglu"]
+    achieved = w13_flops(sp) / (w13_ms * 1e-3) / 1e12
+    down_tf = 2.0 * sp.T * sp.k * sp.I * sp.H / (kern["down"] * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, near-uniform routing)",
+        "tokens_per_s": round(sp.T / (ms * 1e-3), 1),
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "config": {"workload": "denoise MoE layer, 1 micro-shard: T=4096 image tokens, hidden 4096, "
+                               "64 experts top-8, TP2-shard intermediate 1536 (w13 [64,3072,4096], "
+                               "down [64,4096,1536])",
+                   "T": sp.T, "H": sp.H, "E": sp.E, "k": sp.k, "I": sp.I, "micro_count": sp.micro,
+                   "parallelism": "single GPU (one TP2 rank's shard)"},
+        "roofline": {"kernel": "grouped_gemm_bf16<w13> (gate|up GEMM + SwiGLU)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(w13_ms, 5),
+                     "algorithmic_flops_per_launch": w13_flops(sp)},
+        "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
+        "down_gemm_tflops": round(down_tf, 2),
+        "expert_loads": {"min": int(counts.min()), "max": int(counts.max())},
+    }
+    del buf
+
+    if not args.no_extra:
+        extra = {}
+        # 2-micro denoise (same weights, micro-major)
+        sp2 = mi.spec(2)
+        w1, w2 = relayout_two_micro(base, sp2)
+        del d
+        torch.cuda.empty_cache()
+        d2 = upload(mi.LayerInputs(sp2, base.x, base.wg, base.bias, w1, w2), torch)
+        ms2, _, b2 = time_forward(moe, torch, d2, args.steps, args.warmup)
+        extra["denoise_2micro"] = {"ms": round(ms2, 4),
+                                   "tflops": round(expert_flops(sp2) / (ms2 * 1e-3) / 1e12, 2),
+                                   "tokens_per_s": round(sp2.T / (ms2 * 1e-3), 1)}
+        log(f"2-micro {ms2:.4f} ms")
+        del b2
+        # skewed CFG batch (same 2-micro weights, T=8192, Zipf bias)
+        sp4 = mi.spec(4)
+        wg4, bias4 = mi.make_router(sp4)
+        d4 = dict(x=dev(mi.make_x(sp4), torch), wg=dev(wg4, torch), bias=dev(bias4, torch),
+                  w1=d2["w1"], w2=d2["w2"], sp=sp4)
+        ms4, _, b4buf = time_forward(moe, torch, d4, max(3, args.steps // 2), args.warmup)
+        c4 = b4buf.views()["counts"].cpu().numpy()
+        extra["skewed_cfg"] = {"ms": round(ms4, 4),
+                               "tflops": round(expert_flops(sp4) / (ms4 * 1e-3) / 1e12, 2),
+                               "tokens_per_s": round(sp4.T / (ms4 * 1e-3), 1),
+                               "max_load": int(c4.max()), "empty_experts": int((c4 == 0).sum())}
+        log(f"skewed {ms4:.4f} ms")
+        del d2, d4, b4buf
+        torch.cuda.empty_cache()
+        # AR decode
+        sp3 = mi.spec(3)
+        d3 = upload(mi.make_layer(sp3), torch)
+        ms3, _, b3 = time_forward(moe, torch, d3, max(args.steps, 50), args.warmup)
+        n_active = int((b3.views()["counts"].cpu().numpy() > 0).sum())
+        gbs = decode_bytes(sp3, n_active) / (ms3 * 1e-3) / 1e9
+        extra["decode"] = {"ms": round(ms3, 5), "GB_per_s": round(gbs, 1),
+                           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "active_experts": n_active,
+                           "algorithmic_bytes": decode_bytes(sp3, n_active)}
+        log(f"decode {ms3 * 1e3:.1f} us, {gbs:.0f} GB/s, {n_active} active experts")
+        res["other_layers"] = extra
+
+    if not args.no_cpu:
+        log(f"CPU oracle on {args.cpu_tokens} tokens")
+        res["cpu_baseline"] = cpu_baseline(base, args.cpu_tokens)
+
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,148 @@
+"""ctypes binding of libmoe_mi355x.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors, which supply device memory; the current torch stream is passed as
+the HIP stream.  Every step of the layer runs in the library's HIP kernels:
+if the library is missing this module raises on import instead of falling
+back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+EXPORTED = (
+    "moe_status_string", "moe_workspace_size", "moe_get_workspace_layout", "moe_route",
+    "moe_permute", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_down", "moe_finalize",
+    "moe_forward",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)}")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("Im", ctypes.c_int32), ("micro_count", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class MoeWorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("logits", "topk_ids", "topk_w", "counts", "offsets", "perm", "inv", "h", "y",
+                 "total")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m mixture_experts_ffn_moe_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    S = ctypes.POINTER(MoeShape)
+    i32 = ctypes.c_int32
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_workspace_size.argtypes = [S]
+    lib.moe_workspace_size.restype = ctypes.c_size_t
+    lib.moe_get_workspace_layout.argtypes = [S, ctypes.POINTER(MoeWorkspaceLayout)]
+    lib.moe_get_workspace_layout.restype = i32
+    lib.moe_route.argtypes = [S, P, P, P, P, P, P, P]
+    lib.moe_route.restype = i32
+    lib.moe_permute.argtypes = [S, P, P, P, P, P, P, P, P]
+    lib.moe_permute.restype = i32
+    lib.moe_grouped_gemm_w13_swiglu.argtypes = [S, P, P, P, P, P, P]
+    lib.moe_grouped_gemm_w13_swiglu.restype = i32
+    lib.moe_grouped_gemm_down.argtypes = [S, P, P, P, P, P]
+    lib.moe_grouped_gemm_down.restype = i32
+    lib.moe_finalize.argtypes = [S, P, P, P, P, P]
+    lib.moe_finalize.restype = i32
+    lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_forward.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.moe_status_string(code).decode()
+
+
+def make_shape(T, H, E, k, Im, micro_count=1, dtype="bf16") -> MoeShape:
+    d = {"bf16": MOE_BF16, "f32": MOE_F32, MOE_BF16: MOE_BF16, MOE_F32: MOE_F32}[dtype]
+    return MoeShape(T, H, E, k, Im, micro_count, d)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(code: int, where: str):
+    if code != MOE_OK:
+        raise MoeError(code, where)
+
+
+def moe_workspace_size(shape: MoeShape) -> int:
+    return int(lib.moe_workspace_size(ctypes.byref(shape)))
+
+
+def moe_get_workspace_layout(shape: MoeShape) -> dict:
+    L = MoeWorkspaceLayout()
+    _check(lib.moe_get_workspace_layout(ctypes.byref(shape), ctypes.byref(L)), "moe_get_workspace_layout")
+    return {n: int(getattr(L, n)) for n, _ in MoeWorkspaceLayout._fields_}
+
+
+def moe_route(shape, x, wg, bias, logits, topk_ids, topk_w, stream=None):
+    _check(lib.moe_route(ctypes.byref(shape), _ptr(x), _ptr(wg), _ptr(bias), _ptr(logits),
+                         _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "moe_route")
+
+
+def moe_permute(shape, topk_ids, counts, offsets, perm, inv, x=None, permuted_x=None, stream=None):
+    _check(lib.moe_permute(ctypes.byref(shape), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                           _ptr(perm), _ptr(inv), _ptr(x), _ptr(permuted_x), _stream(stream)),
+           "moe_permute")
+
+
+def moe_grouped_gemm_w13_swiglu(shape, x, perm, offsets, w1, h, stream=None):
+    _check(lib.moe_grouped_gemm_w13_swiglu(ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(offsets),
+                                           _ptr(w1), _ptr(h), _stream(stream)),
+           "moe_grouped_gemm_w13_swiglu")
+
+
+def moe_grouped_gemm_down(shape, h, offsets, w2, y, stream=None):
+    _check(lib.moe_grouped_gemm_down(ctypes.byref(shape), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(y),
+                                     _stream(stream)), "moe_grouped_gemm_down")
+
+
+def moe_finalize(shape, y, inv, topk_w, out, stream=None):
+    _check(lib.moe_finalize(ctypes.byref(shape), _ptr(y), _ptr(inv), _ptr(topk_w), _ptr(out),
+                            _stream(stream)), "moe_finalize")
+
+
+def moe_forward(shape, x, wg, bias, w1, w2, out, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.moe_forward(ctypes.byref(shape), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w2),
+                           _ptr(out), _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream)),
+           "moe_forward")

@@ -1,0 +1,60 @@
+// Finalize: routing scale and top-k reduction, once per token.
+//
+// "Hunyuan Image 3.0 hybrid parallelism", section 6.1: finalize reads the
+// expert outputs by original token and top-k slot through the inverse
+// permutation, applies the routing score once and reduces the top-k routes
+// once.  The micro-shard partials were already summed in the down GEMM's fp32
+// accumulator, so each route contributes one row of y.
+//
+// out[t, :] = sum_{j ascending} w[t, j] * y[inv[t*k + j], :] in fp32, one
+// rounding.  No atomics: every output element is owned by one thread, so the
+// result is bitwise reproducible.  One workgroup per token; each thread moves
+// 16-byte vectors, so every row read is fully coalesced.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ y,
+                                                       const int32_t* __restrict__ inv,
+                                                       const float* __restrict__ w, int H, int k,
+                                                       T* __restrict__ out) {
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
+  const int t = blockIdx.x;
+  const int32_t* rows = inv + (size_t)t * k;
+  const float* wt = w + (size_t)t * k;
+  for (int c = threadIdx.x * V; c < H; c += blockDim.x * V) {
+    float acc[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float s = wt[j];
+      const T* src = y + (size_t)rows[j] * H + c;
+      const uint4 raw = *reinterpret_cast<const uint4*>(src);
+      const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] = fmaf(s, Elem<T>::to_f(v[q]), acc[q]);
+    }
+    uint4 res;
+    T* o = reinterpret_cast<T*>(&res);
+#pragma unroll
+    for (int q = 0; q < V; ++q) o[q] = Elem<T>::from_f(acc[q]);
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = res;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const Shape& s, const void* y, const int32_t* inv, const float* w,
+                           void* out, hipStream_t st) {
+  if (s.bf16)
+    hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3(s.T), dim3(256), 0, st,
+                       (const uint16_t*)y, inv, w, s.H, s.k, (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(finalize_kernel<float>, dim3(s.T), dim3(256), 0, st, (const float*)y, inv,
+                       w, s.H, s.k, (float*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,199 @@
+// C ABI of the MoE library: host-side validation, workspace layout and the
+// launch sequence.  Declarations and argument semantics: moe_mi355x.h.
+//
+// Every entry point validates everything it can on the host before any HIP
+// call, so a rejected call enqueues nothing and touches no output.
+#include "../../include/moe_mi355x.h"
+#include "moe_common.h"
+
+using moe::Shape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by every entry point.
+moe_status check_shape(const moe_shape* sh, Shape* out) {
+  if (sh == nullptr) return MOE_ERR_INVALID_ARG;
+  const moe_shape& s = *sh;
+  if (s.T < 0 || s.H <= 0 || s.E <= 0 || s.k <= 0 || s.Im <= 0 || s.micro_count <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s.k > s.E) return MOE_ERR_INVALID_ARG;
+  if (s.dtype != MOE_F32 && s.dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.E > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s.H % 256 != 0 || s.Im % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long R = (long long)s.T * s.k;
+  const long long I = (long long)s.micro_count * s.Im;
+  const long long lim = (1ll << 31) - 1;
+  if (R > lim || I > lim || R * s.H > lim || R * I > lim || (long long)s.T * s.H > lim ||
+      (long long)s.micro_count * s.E * 2 * s.Im * s.H > lim * 8)
+    return MOE_ERR_UNSUPPORTED;
+  if (out) {
+    out->T = s.T; out->H = s.H; out->E = s.E; out->k = s.k; out->Im = s.Im;
+    out->mu = s.micro_count; out->bf16 = (s.dtype == MOE_BF16);
+  }
+  return MOE_OK;
+}
+
+// Non-null and 16-byte aligned (the kernels move 16-byte vectors).
+moe_status check_ptr(const void* p) {
+  if (p == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+#define MOE_CHECK(expr)                 \
+  do {                                  \
+    const moe_status st_ = (expr);      \
+    if (st_ != MOE_OK) return st_;      \
+  } while (0)
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+inline size_t elem_bytes(const Shape& s) { return s.bf16 ? 2 : 4; }
+
+void layout_of(const Shape& s, moe_workspace_layout* L) {
+  const size_t R = (size_t)s.R();
+  size_t o = 0;
+  L->logits = o;   o = align_up(o + (size_t)s.T * s.E * 4);
+  L->topk_ids = o; o = align_up(o + R * 4);
+  L->topk_w = o;   o = align_up(o + R * 4);
+  L->counts = o;   o = align_up(o + (size_t)s.E * 4);
+  L->offsets = o;  o = align_up(o + (size_t)(s.E + 1) * 4);
+  L->perm = o;     o = align_up(o + R * 4);
+  L->inv = o;      o = align_up(o + R * 4);
+  L->h = o;        o = align_up(o + R * (size_t)s.mu * s.Im * elem_bytes(s));
+  L->y = o;        o = align_up(o + R * (size_t)s.H * elem_bytes(s));
+  L->total = o;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported envelope or misaligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+size_t moe_workspace_size(const moe_shape* shape) {
+  Shape s;
+  if (check_shape(shape, &s) != MOE_OK) return 0;
+  moe_workspace_layout L;
+  layout_of(s, &L);
+  return L.total;
+}
+
+moe_status moe_get_workspace_layout(const moe_shape* shape, moe_workspace_layout* layout) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (layout == nullptr) return MOE_ERR_INVALID_ARG;
+  layout_of(s, layout);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const float* wg, const float* bias,
+                     float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(wg)); MOE_CHECK(check_ptr(logits));
+  MOE_CHECK(check_ptr(topk_ids)); MOE_CHECK(check_ptr(topk_w));
+  if (bias != nullptr) MOE_CHECK(check_ptr(bias));
+  return hip_status(moe::launch_route(s, x, wg, bias, logits, topk_ids, topk_w, (hipStream_t)stream));
+}
+
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, const void* x,
+                       void* permuted_x, void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  MOE_CHECK(check_ptr(counts)); MOE_CHECK(check_ptr(offsets));
+  if ((x == nullptr) != (permuted_x == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (s.T == 0) {
+    return MOE_OK;
+  }
+  MOE_CHECK(check_ptr(topk_ids)); MOE_CHECK(check_ptr(perm)); MOE_CHECK(check_ptr(inv));
+  if (x != nullptr) { MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(permuted_x)); }
+  hipStream_t st = (hipStream_t)stream;
+  MOE_CHECK(hip_status(moe::launch_permute(s, topk_ids, counts, offsets, perm, inv, st)));
+  if (x != nullptr) MOE_CHECK(hip_status(moe::launch_gather(s, x, perm, permuted_x, st)));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_gemm_w13_swiglu(const moe_shape* shape, const void* x, const int32_t* perm,
+                                       const int32_t* offsets, const void* w1, void* h,
+                                       void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(perm)); MOE_CHECK(check_ptr(offsets));
+  MOE_CHECK(check_ptr(w1)); MOE_CHECK(check_ptr(h));
+  return hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, (hipStream_t)stream));
+}
+
+moe_status moe_grouped_gemm_down(const moe_shape* shape, const void* h, const int32_t* offsets,
+                                 const void* w2, void* y, void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(h)); MOE_CHECK(check_ptr(offsets)); MOE_CHECK(check_ptr(w2));
+  MOE_CHECK(check_ptr(y));
+  return hip_status(moe::launch_down(s, h, offsets, w2, y, (hipStream_t)stream));
+}
+
+moe_status moe_finalize(const moe_shape* shape, const void* y, const int32_t* inv,
+                        const float* topk_w, void* out, void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(y)); MOE_CHECK(check_ptr(inv)); MOE_CHECK(check_ptr(topk_w));
+  MOE_CHECK(check_ptr(out));
+  return hip_status(moe::launch_finalize(s, y, inv, topk_w, out, (hipStream_t)stream));
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, const float* bias,
+                       const void* w1, const void* w2, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(wg)); MOE_CHECK(check_ptr(w1));
+  MOE_CHECK(check_ptr(w2)); MOE_CHECK(check_ptr(out));
+  if (bias != nullptr) MOE_CHECK(check_ptr(bias));
+  moe_workspace_layout L;
+  layout_of(s, &L);
+  if (workspace == nullptr || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOE_ERR_UNSUPPORTED;
+
+  char* ws = (char*)workspace;
+  float* logits = (float*)(ws + L.logits);
+  int32_t* ids = (int32_t*)(ws + L.topk_ids);
+  float* w = (float*)(ws + L.topk_w);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  int32_t* inv = (int32_t*)(ws + L.inv);
+  void* h = ws + L.h;
+  void* y = ws + L.y;
+  hipStream_t st = (hipStream_t)stream;
+
+  MOE_CHECK(hip_status(moe::launch_route(s, x, wg, bias, logits, ids, w, st)));
+  MOE_CHECK(hip_status(moe::launch_permute(s, ids, counts, offsets, perm, inv, st)));
+  MOE_CHECK(hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, st)));
+  MOE_CHECK(hip_status(moe::launch_down(s, h, offsets, w2, y, st)));
+  MOE_CHECK(hip_status(moe::launch_finalize(s, y, inv, w, out, st)));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Shared device helpers and the internal launcher interface of the MoE
+// kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 64;  // one lane per expert in the top-k wave
+constexpr int kXcds = 8;         // MI355X: 8 accelerator dies, 32 CUs each
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// SiLU(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// Element loads/stores for the two supported element types.  bf16 tensors
+// are moved as raw 16-bit patterns.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_bits_to_float(*p); }
+  static __device__ __forceinline__ float to_f(uint16_t v) { return bf16_bits_to_float(v); }
+  static __device__ __forceinline__ uint16_t from_f(float v) { return float_to_bf16_bits(v); }
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (host side).  Shapes are validated by the caller; every launcher
+// only enqueues on `stream` and returns the launch status.
+
+struct Shape {
+  int T, H, E, k, Im, mu;
+  bool bf16;
+  long long R() const { return (long long)T * k; }
+};
+
+hipError_t launch_route(const Shape& s, const void* x, const float* wg, const float* bias,
+                        float* logits, int32_t* ids, float* w, hipStream_t st);
+
+hipError_t launch_permute(const Shape& s, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* inv, hipStream_t st);
+
+hipError_t launch_gather(const Shape& s, const void* x, const int32_t* perm, void* xp,
+                         hipStream_t st);
+
+hipError_t launch_w13_swiglu(const Shape& s, const void* x, const int32_t* perm,
+                             const int32_t* offsets, const void* w1, void* h, hipStream_t st);
+
+hipError_t launch_down(const Shape& s, const void* h, const int32_t* offsets, const void* w2,
+                       void* y, hipStream_t st);
+
+hipError_t launch_finalize(const Shape& s, const void* y, const int32_t* inv, const float* w,
+                           void* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,53 @@
+"""Tensor-level convenience over the C ABI: allocate a layer call's output and
+workspace with torch and expose the workspace's intermediates as views."""
+from __future__ import annotations
+
+import torch
+
+from ._lib import MOE_BF16, moe_forward, moe_get_workspace_layout, moe_workspace_size
+
+
+def _dtype(shape) -> torch.dtype:
+    return torch.bfloat16 if shape.dtype == MOE_BF16 else torch.float32
+
+
+def workspace_views(shape, ws: torch.Tensor) -> dict:
+    """Views of the intermediates moe_forward leaves in workspace `ws` (uint8)."""
+    L = moe_get_workspace_layout(shape)
+    T, E, k, H = shape.T, shape.E, shape.k, shape.H
+    R = T * k
+    I = shape.micro_count * shape.Im
+    dt = _dtype(shape)
+    es = 2 if dt == torch.bfloat16 else 4
+
+    def view(name, n, elem, dtype, dims):
+        off = L[name]
+        return ws[off:off + n * elem].view(dtype).view(*dims)
+
+    return {
+        "logits": view("logits", T * E, 4, torch.float32, (T, E)),
+        "ids": view("topk_ids", R, 4, torch.int32, (T, k)),
+        "w": view("topk_w", R, 4, torch.float32, (T, k)),
+        "counts": view("counts", E, 4, torch.int32, (E,)),
+        "offsets": view("offsets", E + 1, 4, torch.int32, (E + 1,)),
+        "perm": view("perm", R, 4, torch.int32, (R,)),
+        "inv": view("inv", R, 4, torch.int32, (R,)),
+        "h": view("h", R * I, es, dt, (R, I)),
+        "y": view("y", R * H, es, dt, (R, H)),
+    }
+
+
+class MoELayerBuffers:
+    """Output and workspace of one layer shape, allocated once with torch."""
+
+    def __init__(self, shape, device="cuda"):
+        self.shape = shape
+        self.workspace = torch.empty(moe_workspace_size(shape), dtype=torch.uint8, device=device)
+        self.out = torch.empty(shape.T, shape.H, dtype=_dtype(shape), device=device)
+
+    def forward(self, x, wg, bias, w1, w2, stream=None) -> torch.Tensor:
+        moe_forward(self.shape, x, wg, bias, w1, w2, self.out, self.workspace, stream)
+        return self.out
+
+    def views(self) -> dict:
+        return workspace_views(self.shape, self.workspace)

@@ -1,0 +1,79 @@
+"""Shared test helpers: move seeded inputs to the device, read results back,
+and the parity bars."""
+from __future__ import annotations
+
+import numpy as np
+
+import moe_inputs as mi
+
+# Output tolerances of the workload: bf16 layers max-abs 2e-2 and relative
+# L2 1e-2; the fp32 layer 1e-5 for both.
+TOL = {mi.BF16: (2e-2, 1e-2), mi.F32: (1e-5, 1e-5)}
+
+
+def to_dev(a: np.ndarray, dtype: str, device="cuda"):
+    import torch
+    if dtype == mi.BF16 and a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host_f32(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return mi.bf16_bits_to_f32(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.detach().cpu().numpy()
+
+
+def device_inputs(inp: mi.LayerInputs, device="cuda") -> dict:
+    import torch
+    sp = inp.spec
+    d = {
+        "x": to_dev(inp.x, sp.dtype, device),
+        "wg": torch.from_numpy(inp.wg).to(device),
+        "bias": None if inp.bias is None else torch.from_numpy(inp.bias).to(device),
+        "w1": to_dev(inp.w1, sp.dtype, device),
+        "w2": to_dev(inp.w2, sp.dtype, device),
+    }
+    return d
+
+
+def shape_of(sp: mi.LayerSpec):
+    from mixture_experts_ffn_moe_amd import make_shape
+    return make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
+
+
+def out_dtype(sp):
+    import torch
+    return torch.bfloat16 if sp.dtype == mi.BF16 else torch.float32
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d) / den) if den > 0 else float(np.linalg.norm(d))
+    return max_abs, rel
+
+
+def assert_close(got, ref, dtype: str, what: str = "out"):
+    ma, rl = errors(got, ref)
+    tol_abs, tol_rel = TOL[dtype]
+    assert ma <= tol_abs and rl <= tol_rel, f"{what}: max-abs {ma:.3e} (<= {tol_abs}), rel-L2 {rl:.3e} (<= {tol_rel})"
+    return ma, rl
+
+
+def assert_close_scaled(got, ref, dtype: str, what: str):
+    """Intermediates (h, y) of magnitude up to ~10: per-element bound scaled
+    by the reference magnitude, plus the relative L2 bar."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    tol_abs, tol_rel = TOL[dtype]
+    d = np.abs(got - ref)
+    bound = tol_abs + tol_rel * np.abs(ref)
+    bad = d > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements off, worst {float((d - bound).max()):.3e}"
+    _, rl = errors(got, ref)
+    assert rl <= tol_rel, f"{what}: rel-L2 {rl:.3e}"

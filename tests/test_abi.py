@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and its host-side validation rejects bad calls before any launch.
+
+Every call below fails validation (or has T == 0) on the host, so no kernel is
+ever launched with the placeholder pointers used here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mixture_experts_ffn_moe_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_down",
+              "moe_finalize", "moe_forward", "moe_workspace_size", "moe_status_string",
+              "moe_get_workspace_layout"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(m):
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(m.EXPORTED)
+
+
+def test_status_strings(m):
+    for c in range(5):
+        assert m.status_string(c).startswith("MOE_")
+    assert "unknown" in m.status_string(99)
+
+
+def test_workspace_size_and_layout(m):
+    s = m.make_shape(4096, 4096, 64, 8, 1536, 1, "bf16")
+    L = m.moe_get_workspace_layout(s)
+    R = 4096 * 8
+    assert L["total"] == m.moe_workspace_size(s)
+    assert L["h"] - L["inv"] >= R * 4 and L["y"] - L["h"] >= R * 1536 * 2
+    assert L["total"] - L["y"] >= R * 4096 * 2
+    for v in L.values():
+        assert v % 256 == 0
+    # micro split does not change the size
+    assert m.moe_workspace_size(m.make_shape(4096, 4096, 64, 8, 768, 2, "bf16")) == L["total"]
+    # fp32 intermediates are twice as wide
+    assert m.moe_workspace_size(m.make_shape(64, 256, 8, 2, 128, 1, "f32")) > \
+        m.moe_workspace_size(m.make_shape(64, 256, 8, 2, 128, 1, "bf16"))
+
+
+@pytest.mark.parametrize("args,code", [
+    ((64, 256, 65, 2, 128, 1), "MOE_ERR_UNSUPPORTED"),    # E > 64
+    ((64, 256, 8, 9, 128, 1), "MOE_ERR_INVALID_ARG"),     # k > E
+    ((64, 256, 8, 0, 128, 1), "MOE_ERR_INVALID_ARG"),     # k < 1
+    ((-1, 256, 8, 2, 128, 1), "MOE_ERR_INVALID_ARG"),     # T < 0
+    ((64, 256, 8, 2, 128, 0), "MOE_ERR_INVALID_ARG"),     # no micro-shard
+    ((64, 200, 8, 2, 128, 1), "MOE_ERR_UNSUPPORTED"),     # H not a multiple of 256
+    ((64, 256, 8, 2, 96, 1), "MOE_ERR_UNSUPPORTED"),      # Im not a multiple of 128
+    ((1 << 28, 4096, 64, 8, 128, 1), "MOE_ERR_UNSUPPORTED"),  # T*k*H beyond 2^31
+])
+def test_shape_validation(m, args, code):
+    s = m.make_shape(*args, dtype="bf16")
+    assert m.moe_workspace_size(s) == 0
+    want = getattr(m, code)
+    lib = m._lib.lib
+    P = ctypes.c_void_p(4096)  # placeholder, never dereferenced: validation fails first
+    assert lib.moe_forward(ctypes.byref(s), P, P, None, P, P, P, P, ctypes.c_size_t(1 << 40), None) == want
+    assert lib.moe_route(ctypes.byref(s), P, P, None, P, P, P, None) == want
+    assert lib.moe_finalize(ctypes.byref(s), P, P, P, P, None) == want
+
+
+def test_bad_dtype_and_null_shape(m):
+    s = m.MoeShape(64, 256, 8, 2, 128, 1, 7)
+    lib = m._lib.lib
+    P = ctypes.c_void_p(4096)
+    assert lib.moe_grouped_gemm_down(ctypes.byref(s), P, P, P, P, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(None, P, P, None, P, P, P, P, ctypes.c_size_t(1 << 40), None) == m.MOE_ERR_INVALID_ARG
+
+
+def test_pointer_and_workspace_validation(m):
+    lib = m._lib.lib
+    s = m.make_shape(64, 256, 8, 2, 128, 1, "bf16")
+    need = m.moe_workspace_size(s)
+    P = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    ws = ctypes.c_void_p(1 << 20)
+    # null input
+    assert lib.moe_forward(ctypes.byref(s), None, P, None, P, P, P, ws, need, None) == m.MOE_ERR_INVALID_ARG
+    # misaligned weight
+    assert lib.moe_forward(ctypes.byref(s), P, P, None, mis, P, P, ws, need, None) == m.MOE_ERR_UNSUPPORTED
+    # workspace too small / missing / misaligned
+    assert lib.moe_forward(ctypes.byref(s), P, P, None, P, P, P, ws, need - 1, None) == m.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(ctypes.byref(s), P, P, None, P, P, P, None, need, None) == m.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(ctypes.byref(s), P, P, None, P, P, P, ctypes.c_void_p((1 << 20) + 16), need, None) \
+        == m.MOE_ERR_UNSUPPORTED
+    # permute: x and permuted_x must come together
+    assert lib.moe_permute(ctypes.byref(s), P, P, P, P, P, P, None, None) == m.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_no_op(m):
+    lib = m._lib.lib
+    s = m.make_shape(0, 256, 8, 2, 128, 1, "bf16")
+    P = ctypes.c_void_p(4096)
+    assert lib.moe_forward(ctypes.byref(s), P, P, None, P, P, P, P, ctypes.c_size_t(0), None) == m.MOE_OK
+    assert lib.moe_route(ctypes.byref(s), P, P, None, P, P, P, None) == m.MOE_OK
+    assert lib.moe_grouped_gemm_w13_swiglu(ctypes.byref(s), P, P, P, P, P, None) == m.MOE_OK
+
+
+def test_binding_raises_on_error(m):
+    s = m.make_shape(64, 256, 65, 2, 128, 1, "bf16")
+    with pytest.raises(m.MoeError) as ei:
+        m._lib._check(m._lib.lib.moe_route(ctypes.byref(s), None, None, None, None, None, None, None), "moe_route")
+    assert ei.value.code == m.MOE_ERR_UNSUPPORTED

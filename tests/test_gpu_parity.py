@@ -1,0 +1,304 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Routing (logits, ids), counts, offsets, the permutation and its inverse, and
+the gathered input are compared bit for bit; weights and activations within
+the workload's tolerances.  Small layers are compared element by element;
+the full-size layers on every routing field and on sampled output rows,
+which the oracle evaluates token by token."""
+import sys
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle as o
+from helpers import (TOL, assert_close, assert_close_scaled, device_inputs, errors, out_dtype,
+                     shape_of, to_dev, to_host_f32)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+torch = pytest.importorskip("torch")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_ffn_moe_amd as m
+    return m
+
+
+def run_steps(m, sp, d):
+    """Run the five step-wise entry points; return all device results."""
+    s = shape_of(sp)
+    T, E, k, H, R = sp.T, sp.E, sp.k, sp.H, sp.T * sp.k
+    dev = d["x"].device
+    r = {
+        "logits": torch.empty(T, E, dtype=torch.float32, device=dev),
+        "ids": torch.empty(T, k, dtype=torch.int32, device=dev),
+        "w": torch.empty(T, k, dtype=torch.float32, device=dev),
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "perm": torch.empty(R, dtype=torch.int32, device=dev),
+        "inv": torch.empty(R, dtype=torch.int32, device=dev),
+        "h": torch.empty(R, sp.micro * sp.Im, dtype=out_dtype(sp), device=dev),
+        "y": torch.empty(R, H, dtype=out_dtype(sp), device=dev),
+        "out": torch.empty(T, H, dtype=out_dtype(sp), device=dev),
+    }
+    m.moe_route(s, d["x"], d["wg"], d["bias"], r["logits"], r["ids"], r["w"])
+    m.moe_permute(s, r["ids"], r["counts"], r["offsets"], r["perm"], r["inv"])
+    m.moe_grouped_gemm_w13_swiglu(s, d["x"], r["perm"], r["offsets"], d["w1"], r["h"])
+    m.moe_grouped_gemm_down(s, r["h"], r["offsets"], d["w2"], r["y"])
+    m.moe_finalize(s, r["y"], r["inv"], r["w"], r["out"])
+    torch.cuda.synchronize()
+    return r
+
+
+def check_routing(sp, inp, got, ref):
+    """Bit-exact routing fields (logits except oracle-flagged near-midpoint
+    values, whose ids are then checked against the GPU's own logits)."""
+    L = got["logits"].cpu().numpy()
+    flags = o.logits_near_midpoint(o.widen(inp.x, sp.dtype), inp.wg, inp.bias)
+    same = (L.view(np.uint32) == ref["logits"].view(np.uint32)) | flags
+    assert same.all(), f"{int((~same).sum())} logits differ"
+    ids = got["ids"].cpu().numpy()
+    if flags.any():
+        ref_ids = o.select_topk(L, sp.k)
+    else:
+        ref_ids = ref["ids"]
+        assert np.array_equal(L.view(np.uint32), ref["logits"].view(np.uint32))
+    assert np.array_equal(ids, ref_ids)
+    w = got["w"].cpu().numpy()
+    np.testing.assert_allclose(w, o.topk_weights(L, ids), rtol=2e-6, atol=1e-7)
+    counts = o.expert_counts(ids, sp.E)
+    perm, inv = o.route_permutation(ids)
+    assert np.array_equal(got["counts"].cpu().numpy(), counts)
+    assert np.array_equal(got["offsets"].cpu().numpy(), o.expert_offsets(counts))
+    assert np.array_equal(got["perm"].cpu().numpy(), perm)
+    assert np.array_equal(got["inv"].cpu().numpy(), inv)
+
+
+# ------------------------------------------------------------------ small layers
+
+SMALL = [
+    dict(name="tiny_fp32", cfg=0),
+    dict(name="bf16_one_tile", T=300, H=256, E=8, k=2, Im=128, micro=2, dtype=mi.BF16, seed=11),
+    dict(name="bf16_ragged", T=1000, H=512, E=6, k=3, Im=256, micro=1, dtype=mi.BF16, seed=12),
+    dict(name="bf16_skewed_empty", T=700, H=256, E=16, k=4, Im=128, micro=2, dtype=mi.BF16, seed=13,
+         zipf={"s": 1.2, "scale": 6.0, "seed": 13}),
+    dict(name="f32_two_micro", T=200, H=256, E=8, k=2, Im=128, micro=2, dtype=mi.F32, seed=14),
+    dict(name="f32_skewed", T=150, H=256, E=12, k=3, Im=128, micro=1, dtype=mi.F32, seed=15,
+         zipf={"s": 1.2, "scale": 6.0, "seed": 15}),
+    dict(name="one_token_all_experts", T=1, H=256, E=64, k=64, Im=128, micro=1, dtype=mi.BF16, seed=16),
+    dict(name="k1_many_tokens", T=2000, H=256, E=64, k=1, Im=128, micro=1, dtype=mi.BF16, seed=17),
+]
+
+
+def small_spec(c):
+    c = dict(c)
+    name = c.pop("name")
+    if "cfg" in c:
+        return mi.spec(c["cfg"])
+    zipf = c.pop("zipf", None)
+    sp = mi.custom_spec(zipf=zipf, name=name, **c)
+    return sp
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c["name"] for c in SMALL])
+def test_small_layer_stepwise_and_forward(m, case):
+    sp = small_spec(case)
+    say(f"[parity] small layer {case['name']}: T={sp.T} H={sp.H} E={sp.E} k={sp.k} Im={sp.Im} mu={sp.micro} {sp.dtype}")
+    inp = mi.make_layer(sp)
+    ref = o.forward(inp)
+    d = device_inputs(inp)
+    got = run_steps(m, sp, d)
+    check_routing(sp, inp, got, ref)
+    # gathered input, bit for bit
+    s = shape_of(sp)
+    xp = torch.empty(sp.T * sp.k, sp.H, dtype=d["x"].dtype, device="cuda")
+    c2, o2 = torch.empty_like(got["counts"]), torch.empty_like(got["offsets"])
+    p2, i2 = torch.empty_like(got["perm"]), torch.empty_like(got["inv"])
+    m.moe_permute(s, got["ids"], c2, o2, p2, i2, d["x"], xp)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_f32(xp), o.gather_rows(o.widen(inp.x, sp.dtype), ref["perm"], sp.k))
+    # h against the oracle's SwiGLU activations on the same rows
+    Xp = o.gather_rows(o.widen(inp.x, sp.dtype), ref["perm"], sp.k)
+    h_ref = np.zeros((sp.T * sp.k, sp.micro * sp.Im))
+    for e in range(sp.E):
+        a, b = int(ref["offsets"][e]), int(ref["offsets"][e + 1])
+        if a == b:
+            continue
+        w1s, _ = o.expert_weights_f32(inp, e)
+        for mm in range(sp.micro):
+            G = Xp[a:b].astype(np.float64) @ w1s[mm][:sp.Im].T.astype(np.float64)
+            U = Xp[a:b].astype(np.float64) @ w1s[mm][sp.Im:].T.astype(np.float64)
+            h_ref[a:b, mm * sp.Im:(mm + 1) * sp.Im] = o.silu(G) * U
+    assert_close_scaled(to_host_f32(got["h"]), h_ref, sp.dtype, "h")
+    assert_close_scaled(to_host_f32(got["y"]), ref["Y"], sp.dtype, "y")
+    ma, rl = assert_close(to_host_f32(got["out"]), ref["out"], sp.dtype)
+    # one-call path: identical bytes to the step-wise path
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    buf = MoELayerBuffers(s)
+    out = buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                       got["out"].view(torch.int16) if out.dtype == torch.bfloat16 else got["out"])
+    v = buf.views()
+    for f in ("logits", "ids", "w", "counts", "offsets", "perm", "inv"):
+        assert torch.equal(v[f], got[f]), f
+    say(f"[parity] {case['name']}: out max-abs {ma:.2e} rel-L2 {rl:.2e}")
+
+
+def test_tiny_runs_are_bitwise_reproducible(m):
+    sp = mi.spec(0)
+    inp = mi.make_layer(sp)
+    d = device_inputs(inp)
+    a = run_steps(m, sp, d)
+    b = run_steps(m, sp, d)
+    for f in a:
+        assert torch.equal(a[f], b[f]), f
+
+
+def test_non_default_stream(m):
+    sp = small_spec(SMALL[1])
+    inp = mi.make_layer(sp)
+    d = device_inputs(inp)
+    ref = run_steps(m, sp, d)
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    st = torch.cuda.Stream()
+    buf = MoELayerBuffers(shape_of(sp))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        out = buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    st.synchronize()
+    assert torch.equal(out.view(torch.int16), ref["out"].view(torch.int16))
+
+
+def test_routing_ties_toward_lower_expert(m):
+    """Constructed exact ties: x = 1 in one column, router rows with equal
+    values, so several experts share one logit; the lower index must win and
+    -0.0 / +0.0 must compare equal."""
+    T, H, E, k = 4, 256, 8, 3
+    x = np.zeros((T, H), np.float32)
+    x[:, 0] = 1.0
+    wg = np.zeros((E, H), np.float32)
+    wg[:, 0] = [0.5, 2.0, 2.0, -1.0, 2.0, 0.5, -0.0, 0.0]
+    x[3, 0] = -1.0  # token 3 flips every sign: -0.0 and +0.0 both appear
+    s = shape_of(mi.custom_spec(T=T, H=H, E=E, k=k, Im=128, dtype=mi.F32))
+    xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(wg).cuda()
+    L = torch.empty(T, E, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, device="cuda")
+    m.moe_route(s, xd, wd, None, L, ids, w)
+    torch.cuda.synchronize()
+    Lh = L.cpu().numpy()
+    assert np.array_equal(ids.cpu().numpy(), o.brute_rank_topk(Lh, k))
+    assert ids.cpu().numpy()[0].tolist() == [1, 2, 4]
+    assert ids.cpu().numpy()[3].tolist() == [3, 6, 7]
+
+
+# ------------------------------------------------------------------ full-size layers
+
+_CACHE = {}
+
+
+def full_layer(i):
+    """Seeded inputs of config i; configs 1, 2 and 4 share one layer's
+    weights (2 and 4 hold them micro-major), generated once."""
+    if i in _CACHE:
+        return _CACHE[i]
+    sp = mi.spec(i)
+    if i in (2, 4) and 1 in _CACHE:
+        base = _CACHE[1]
+        w1 = np.empty((2, sp.E, 2 * sp.Im, sp.H), np.uint16)
+        w2 = np.empty((2, sp.E, sp.H, sp.Im), np.uint16)
+        I, Im = 1536, 768
+        for mm in range(2):
+            w1[mm, :, :Im] = base.w1[0, :, mm * Im:(mm + 1) * Im]
+            w1[mm, :, Im:] = base.w1[0, :, I + mm * Im:I + (mm + 1) * Im]
+            w2[mm] = base.w2[0, :, :, mm * Im:(mm + 1) * Im]
+        x = base.x if i == 2 else mi.make_x(sp)
+        wg, bias = mi.make_router(sp)
+        inp = mi.LayerInputs(sp, x, wg, bias, w1, w2)
+    else:
+        inp = mi.make_layer(sp)
+    _CACHE[i] = inp
+    return inp
+
+
+def sample_tokens(T, n=16, seed=0):
+    rng = np.random.default_rng(seed)
+    s = set([0, T - 1]) | set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    return sorted(s)
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_full_size_forward(m, i):
+    sp = mi.spec(i)
+    say(f"[parity] full-size config {sp.name}: T={sp.T} E={sp.E} k={sp.k} Im={sp.Im} mu={sp.micro}")
+    inp = full_layer(i)
+    ref = o.route(inp)
+    d = device_inputs(inp)
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    buf = MoELayerBuffers(shape_of(sp))
+    out = buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    v = buf.views()
+    check_routing(sp, inp, v, ref)
+    if i == 4:
+        counts = ref["counts"]
+        assert (counts == 0).any()
+        say(f"[parity] skewed loads: max {counts.max()} empty {(counts == 0).sum()}")
+    toks = sample_tokens(sp.T)
+    want = o.token_outputs(inp, ref, toks)
+    got = to_host_f32(out)[toks]
+    ma, rl = assert_close(got, want, sp.dtype, f"{sp.name} sampled rows")
+    say(f"[parity] {sp.name}: sampled out max-abs {ma:.2e} rel-L2 {rl:.2e}")
+    # run-to-run bitwise reproducibility of the whole call
+    out2 = MoELayerBuffers(shape_of(sp)).forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    _CACHE[f"out{i}"] = to_host_f32(out)
+    del d, buf
+    torch.cuda.empty_cache()
+
+
+def test_two_micro_equals_one_micro_full_size(m):
+    """The 2-micro layer (micro-major pack) must equal the expert-major layer
+    within tolerance over every output element."""
+    if "out1" not in _CACHE or "out2" not in _CACHE:
+        pytest.skip("needs the full-size runs of configs 1 and 2 in this session")
+    assert_close(_CACHE["out2"], _CACHE["out1"], mi.BF16, "2-micro vs 1-micro")
+
+
+def test_micro_views_sum_to_multi_micro(m):
+    """fwd(micro 0 view) + fwd(micro 1 view) = fwd(2-micro), on a bf16 layer
+    of several tiles; the views are plain pointer offsets into the pack.  Each
+    GPU result meets the bar against the oracle; the sum of the two views
+    against the 2-micro result is held to twice the bar, since three
+    independently rounded bf16 outputs enter it."""
+    sp = mi.custom_spec(T=600, H=512, E=8, k=2, Im=256, micro=2, dtype=mi.BF16, seed=21)
+    inp = mi.make_layer(sp)
+    d = device_inputs(inp)
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers, make_shape
+    full = to_host_f32(MoELayerBuffers(shape_of(sp)).forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"]))
+    vs = make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, 1, sp.dtype)
+    view_spec = mi.custom_spec(T=600, H=512, E=8, k=2, Im=256, micro=1, dtype=mi.BF16, seed=21)
+    parts = []
+    for mm in range(2):
+        got = to_host_f32(MoELayerBuffers(vs).forward(d["x"], d["wg"], d["bias"],
+                                                      d["w1"][mm].contiguous(), d["w2"][mm].contiguous()))
+        ref_m = o.forward(mi.LayerInputs(view_spec, inp.x, inp.wg, inp.bias, inp.w1[mm:mm + 1],
+                                         inp.w2[mm:mm + 1]))["out"]
+        assert_close(got, ref_m, mi.BF16, f"micro view {mm}")
+        parts.append(got)
+    torch.cuda.synchronize()
+    ref = o.forward(inp)["out"]
+    assert_close(full, ref, mi.BF16, "2-micro")
+    ma, rl = errors(parts[0] + parts[1], full)
+    assert ma <= 2 * TOL[mi.BF16][0] and rl <= 2 * TOL[mi.BF16][1], (ma, rl)
