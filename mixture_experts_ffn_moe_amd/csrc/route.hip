@@ -11,7 +11,7 @@
 // selected experts reproducible against a CPU evaluation.
 //
 // One workgroup handles kTokTile tokens: the fp64 logit tile [kTokTile x 64]
-// is accumulated over H in LDS-staged chunks, then each wave runs the top-k of
+// is accumulated on the fp64 matrix pipe, then each wave runs the top-k of
 // its tokens with one lane per expert: k rounds of a 64-lane arg-max over the
 // key (orderable(logit) << 32 | (63 - e)), so equal logits go to the lower
 // expert index.
@@ -21,8 +21,6 @@ namespace moe {
 namespace {
 
 constexpr int kTokTile = 16;  // tokens per workgroup
-constexpr int kHChunk = 128;  // hidden elements staged per step
-constexpr int kWsPad = 4;     // floats of padding per staged router row
 
 // Orderable 32-bit key of a float: unsigned order equals numeric order and
 // -0.0 maps to the key of +0.0.
@@ -55,6 +53,31 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive activations of one token as fp32 (exact for bf16 and fp32).
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 r = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Logit tile of kTokTile tokens x 64 experts on the fp64 matrix pipe
+// (v_mfma_f64_16x16x4_f64, exact products, fp64 sums).  Wave w covers the
+// hidden range [w*H/4, (w+1)*H/4) for all four 16-expert tiles; lane
+// (t = lane%16, g = lane/16) holds x[t][h0 + 8g + m] and wg[16q + t][h0 + 8g + m]
+// as the m-th MFMA's A and B elements, so the 8 MFMAs of a 32-wide chunk sum
+// every h of the chunk exactly once.  The four wave partials are added in a
+// fixed order, so the logits are reproducible run to run.
 template <typename XT>
 __global__ __launch_bounds__(256) void route_kernel(const XT* __restrict__ x,
                                                     const float* __restrict__ wg,
@@ -62,64 +85,65 @@ __global__ __launch_bounds__(256) void route_kernel(const XT* __restrict__ x,
                                                     int E, int k, float* __restrict__ logits,
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ topw) {
-  __shared__ __attribute__((aligned(16))) float xs[kTokTile][kHChunk];
-  __shared__ __attribute__((aligned(16))) float ws[kMaxExperts][kHChunk + kWsPad];
+  __shared__ double part[4][kTokTile][kMaxExperts + 1];
   __shared__ float lg[kTokTile][kMaxExperts];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kTokTile;
-  const int e = tid & 63;          // expert of this thread's logits
-  const int tg = tid >> 6;         // token group: tokens tg*4 .. tg*4+3
+  const int tl = lane & 15, g = lane >> 4;
+  const int hq = H / 4;
+  const int hb = wave * hq;
 
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-
-  for (int h0 = 0; h0 < H; h0 += kHChunk) {
-    // x chunk: 16 tokens x 128 values, 8 consecutive values per thread.
-    {
-      const int idx = tid * 8;
-      const int r = idx / kHChunk, c = idx % kHChunk;
-      const int t = t0 + r;
+  const bool tok_ok = t0 + tl < T;
+  const XT* xrow = x + (size_t)min(t0 + tl, T - 1) * H + hb + 8 * g;
+  const float* wrow[4];
+  bool w_ok[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        xs[r][c + q] = (t < T) ? Elem<XT>::to_f(x[(size_t)t * H + h0 + c + q]) : 0.0f;
-    }
-    // router chunk: 64 experts x 128 values, 8 float4 per thread.
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = (tid + q * 256) * 4;
-      const int r = idx / kHChunk, c = idx % kHChunk;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < E) v = *reinterpret_cast<const float4*>(wg + (size_t)r * H + h0 + c);
-      *reinterpret_cast<float4*>(&ws[r][c]) = v;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < kHChunk; c += 4) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&ws[e][c]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 x4 = *reinterpret_cast<const float4*>(&xs[tg * 4 + i][c]);
-        acc[i] = fma((double)x4.x, (double)w4.x, acc[i]);
-        acc[i] = fma((double)x4.y, (double)w4.y, acc[i]);
-        acc[i] = fma((double)x4.z, (double)w4.z, acc[i]);
-        acc[i] = fma((double)x4.w, (double)w4.w, acc[i]);
-      }
-    }
-    __syncthreads();
+  for (int q = 0; q < 4; ++q) {
+    const int e = 16 * q + tl;
+    w_ok[q] = e < E;
+    wrow[q] = wg + (size_t)min(e, E - 1) * H + hb + 8 * g;
   }
 
-  const double b = (bias != nullptr && e < E) ? (double)bias[e] : 0.0;
+  f64x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  for (int c = 0; c < hq; c += 32) {
+    float xv[8], wv[4][8];
+    load8(xrow + c, xv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load8(wrow[q] + c, wv[q]);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const double a = tok_ok ? (double)xv[m] : 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[q][m] : 0.0, acc[q], 0, 0, 0);
+    }
+  }
+  // fp64 16x16 D layout: register r of lane holds row (lane/16) + 4r (token),
+  // column lane%16 (expert)
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][g + 4 * r][16 * q + tl] = acc[q][r];
+  __syncthreads();
+
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = tg * 4 + i, t = t0 + r;
-    const float L = (float)(acc[i] + b);
+    const int idx = tid + 256 * i;
+    const int r = idx >> 6, e = idx & 63;
+    const double s = ((part[0][r][e] + part[1][r][e]) + part[2][r][e]) + part[3][r][e];
+    const double b = (bias != nullptr && e < E) ? (double)bias[e] : 0.0;
+    const float L = (float)(s + b);
     lg[r][e] = L;
-    if (t < T && e < E) logits[(size_t)t * E + e] = L;
+    if (t0 + r < T && e < E) logits[(size_t)(t0 + r) * E + e] = L;
   }
   __syncthreads();
 
   // top-k: wave w handles tokens w*4 .. w*4+3, lane = expert.
-  const int wave = tid >> 6, lane = tid & 63;
   for (int i = 0; i < 4; ++i) {
     const int r = wave * 4 + i, t = t0 + r;
     if (t >= T) break;
