@@ -76,6 +76,7 @@ typedef struct {
   size_t inv;      /* int32   [R]            */
   size_t h;        /* dtype   [R, mu*Im]     */
   size_t y;        /* dtype   [R, H]         */
+  size_t scratch;  /* small-token path: fp64 router partials and the active-expert list */
   size_t total;    /* bytes needed            */
 } moe_workspace_layout;
 
@@ -150,8 +151,14 @@ moe_status moe_finalize(const moe_shape* shape, const void* y, const int32_t* in
  * shard and a single micro view (pass w1/w2 offset to that micro).
  *   workspace: device buffer of at least moe_workspace_size(shape) bytes,
  *   256-byte aligned; its intermediates sit at moe_get_workspace_layout's
- *   offsets.  Small token counts take a weight-streaming path whose results
- *   match the step-wise path within rounding.  Output out [T, H] dtype. */
+ *   offsets.
+ *   Small token counts (T <= 16, bf16, H % 2048 == 0, Im % 256 == 0) take a
+ *   weight-streaming path (the AR-decode regime: hybrid parallelism,
+ *   sections 4.3 and 6.2): routing, counts, offsets, perm and inv are the
+ *   same bits as the step-wise path, h is computed the same way, and the down
+ *   projection is fused with the finalize (no rounding of y to dtype), so the
+ *   output matches the step-wise path within rounding, not bit for bit; the
+ *   y region is then left untouched.  Output out [T, H] dtype. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, const float* bias,
                        const void* w1, const void* w2, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);

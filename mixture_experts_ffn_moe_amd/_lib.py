@@ -42,7 +42,7 @@ class MoeShape(ctypes.Structure):
 class MoeWorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("logits", "topk_ids", "topk_w", "counts", "offsets", "perm", "inv", "h", "y",
-                 "total")]
+                 "scratch", "total")]
 
 
 def _load():

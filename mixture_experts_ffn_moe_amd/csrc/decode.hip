@@ -1,0 +1,360 @@
+// Small-token (AR decode) path of the routed MoE layer.
+//
+// In the AR phase each rank runs the MoE for a handful of tokens on its
+// micro view of the resident shard ("Hunyuan Image 3.0 hybrid parallelism",
+// sections 4.3 and 6.2).  With T <= 16 tokens every expert sees at most T
+// rows, so the layer is a stream over the active experts' weights: the time
+// is the HBM time of those weights, and the job of these kernels is to keep
+// enough bytes in flight and to spend no extra launches or passes.
+//
+//   1. decode_route_partial: fp64 router partial sums, the hidden dimension
+//      split over kSplit workgroups (one CU could not stream the router
+//      weights fast enough), exact products on v_mfma_f64_16x16x4_f64.
+//   2. decode_route_finish (one workgroup): fixed-order sum of the partials,
+//      bias, one fp32 rounding, top-k and weights (same rules as route.hip),
+//      expert counts and offsets, the stable permutation and its inverse, and
+//      the ascending list of active experts.
+//   3. decode_w13: one workgroup per (active expert, 64 columns of the
+//      micro-major intermediate); each wave streams 16 gate and 16 up rows of
+//      w1 straight from memory into MFMA B fragments (M = the expert's rows,
+//      padded to 16) and applies SwiGLU; h is rounded to bf16.
+//   4. decode_down_finalize: one workgroup per 16 output columns; its waves
+//      split the active experts, stream the matching w2 rows, and put
+//      w[t, j] * y[route (t, j)] into a per-route LDS slot; the slots are then
+//      summed in ascending j (the finalize of section 6.1), so the down
+//      partials of every micro-shard and route are reduced once, without
+//      atomics and without a y tensor.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kDecT = 16;       // token tile (max tokens on this path)
+constexpr int kSplit = 16;      // router split of the hidden dimension
+constexpr int kMaxK = 64;
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t orderable(float f) {
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, d);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+__device__ __forceinline__ void load8f(const uint16_t* p, float (&v)[8]) {
+  const uint4 r = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1. router partials: block s covers hidden [s*H/kSplit, (s+1)*H/kSplit), its
+// wave w a quarter of that; partial[s][t][e] (fp64, summed over the waves in
+// a fixed order).
+__global__ __launch_bounds__(256) void decode_route_partial(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ wg, int T,
+                                                            int H, int E,
+                                                            double* __restrict__ partial) {
+  __shared__ double part[4][kDecT][kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tl = lane & 15, g = lane >> 4;
+  const int hs = H / kSplit, hq = hs / 4;
+  const int hb = blockIdx.x * hs + wave * hq;
+  const bool tok_ok = tl < T;
+  const uint16_t* xrow = x + (size_t)min(tl, T - 1) * H + hb + 8 * g;
+  const float* wrow[4];
+  bool w_ok[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 16 * q + tl;
+    w_ok[q] = e < E;
+    wrow[q] = wg + (size_t)min(e, E - 1) * H + hb + 8 * g;
+  }
+  f64x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int c = 0; c < hq; c += 32) {
+    float xv[8], wv[4][8];
+    load8f(xrow + c, xv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a = *reinterpret_cast<const float4*>(wrow[q] + c);
+      const float4 b = *reinterpret_cast<const float4*>(wrow[q] + c + 4);
+      wv[q][0] = a.x; wv[q][1] = a.y; wv[q][2] = a.z; wv[q][3] = a.w;
+      wv[q][4] = b.x; wv[q][5] = b.y; wv[q][6] = b.z; wv[q][7] = b.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const double a = tok_ok ? (double)xv[m] : 0.0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[q][m] : 0.0, acc[q], 0, 0, 0);
+    }
+  }
+  // fp64 16x16 D layout: register r holds row (lane/16) + 4r, column lane%16
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][g + 4 * r][16 * q + tl] = acc[q][r];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx >> 6, e = idx & 63;
+    partial[((size_t)blockIdx.x * kDecT + r) * kMaxExperts + e] =
+        ((part[0][r][e] + part[1][r][e]) + part[2][r][e]) + part[3][r][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. routing of the token tile in one workgroup of 16 waves.
+__global__ __launch_bounds__(1024) void decode_route_finish(
+    const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ topw,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ active) {
+  __shared__ float lg[kDecT][kMaxExperts];
+  __shared__ int sids[kDecT * kMaxK];
+  __shared__ int cnt[kMaxExperts], base[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  {  // logits: thread (r, e), partials summed in split order
+    const int r = tid >> 6, e = tid & 63;
+    double s = 0.0;
+    for (int b = 0; b < kSplit; ++b) s += partial[((size_t)b * kDecT + r) * kMaxExperts + e];
+    const double bb = (bias != nullptr && e < E) ? (double)bias[e] : 0.0;
+    const float L = (float)(s + bb);
+    lg[r][e] = L;
+    if (r < T && e < E) logits[(size_t)r * E + e] = L;
+  }
+  __syncthreads();
+
+  {  // top-k and weights: wave = token, lane = expert
+    const int t = wave;
+    if (t < T) {
+      uint64_t key = 0;
+      if (lane < E) key = ((uint64_t)orderable(lg[t][lane]) << 32) | (uint32_t)(63 - lane);
+      float mine = 0.0f, first = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const uint64_t m = wave_max_u64(key);
+        const int win = 63 - (int)(m & 0xffffffffu);
+        const float Lw = from_orderable((uint32_t)(m >> 32));
+        if (j == 0) first = Lw;
+        if (lane == j) mine = Lw;
+        if (lane == win) key = 0;
+        if (lane == 0) {
+          ids[(size_t)t * k + j] = win;
+          sids[t * k + j] = win;
+        }
+      }
+      const double ex = (lane < k) ? exp((double)mine - (double)first) : 0.0;
+      const double s = wave_sum_f64(ex);
+      if (lane < k) topw[(size_t)t * k + lane] = (float)(ex / s);
+    }
+  }
+  __syncthreads();
+
+  // counts, offsets, active list (wave 0, lane = expert)
+  const int R = T * k;
+  if (wave == 0) {
+    int c = 0;
+    for (int r = 0; r < R; ++r) c += (sids[r] == lane);
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int excl = incl - c;
+    cnt[lane] = c;
+    base[lane] = excl;
+    if (lane < E) {
+      counts[lane] = c;
+      offsets[lane] = excl;
+    }
+    if (lane == E - 1) offsets[E] = incl;
+    // active experts in ascending order: position = number of active experts below
+    const uint64_t act = __ballot(lane < E && c > 0);
+    const uint64_t below = (lane == 0) ? 0ull : (act & ((~0ull) >> (64 - lane)));
+    if (lane < E && c > 0) active[__popcll(below)] = lane;
+    if (lane == 0) active[kMaxExperts] = __popcll(act);
+  }
+  __syncthreads();
+  // stable scatter: route r goes after every earlier route of its expert
+  for (int r = tid; r < R; r += blockDim.x) {
+    const int e = sids[r];
+    int rank = 0;
+    for (int q = 0; q < r; ++q) rank += (sids[q] == e);
+    const int p = base[e] + rank;
+    perm[p] = r;
+    inv[r] = p;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. gate|up + SwiGLU for one active expert and 64 intermediate columns.
+constexpr int kUnroll = 8;  // k-steps of 32 in flight per wave
+
+__global__ __launch_bounds__(256) void decode_w13(const uint16_t* __restrict__ x,
+                                                  const int32_t* __restrict__ perm,
+                                                  const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ active,
+                                                  const uint16_t* __restrict__ w1, int H, int E,
+                                                  int k, int Im, int mu, int ncg,
+                                                  uint16_t* __restrict__ h) {
+  const int a = blockIdx.x / ncg, cg = blockIdx.x % ncg;
+  if (a >= active[kMaxExperts]) return;
+  const int e = active[a];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = offsets[e], n = offsets[e + 1] - seg;
+  const int c0 = cg * 64 + wave * 16;      // column in [0, mu*Im)
+  const int micro = c0 / Im, i0 = c0 - micro * Im;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+
+  const bool row_ok = fr < n;
+  const uint16_t* arow = x + (size_t)(perm[seg + min(fr, n - 1)] / k) * H + fk;
+  const uint16_t* wbase = w1 + (size_t)(micro * E + e) * 2 * Im * H;
+  const uint16_t* grow = wbase + (size_t)(i0 + fr) * H + fk;
+  const uint16_t* urow = wbase + (size_t)(Im + i0 + fr) * H + fk;
+
+  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < H; k0 += 32 * kUnroll) {
+    uint4 av[kUnroll], gv[kUnroll], uv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      gv[u] = *reinterpret_cast<const uint4*>(grow + k0 + 32 * u);
+      uv[u] = *reinterpret_cast<const uint4*>(urow + k0 + 32 * u);
+      av[u] = *reinterpret_cast<const uint4*>(arow + k0 + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint4 aa = av[u];
+      if (!row_ok) aa = make_uint4(0, 0, 0, 0);
+      const bf16x8 A = __builtin_bit_cast(bf16x8, aa);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, gv[u]), accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, uv[u]), accu, 0, 0, 0);
+    }
+  }
+  // D layout: register r holds row 4*(lane/16) + r, column lane%16
+  const int ldh = mu * Im;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (lane >> 4) + r;
+    if (row < n)
+      h[(size_t)(seg + row) * ldh + c0 + fr] = float_to_bf16_bits(silu_f32(accg[r]) * accu[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. down projection + finalize for 16 output columns and all tokens.
+__global__ __launch_bounds__(256) void decode_down_finalize(
+    const uint16_t* __restrict__ h, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
+    const float* __restrict__ topw, const uint16_t* __restrict__ w2, int T, int H, int E, int k,
+    int Im, int mu, uint16_t* __restrict__ out) {
+  __shared__ float slot[kDecT * kMaxK][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const int n_act = active[kMaxExperts];
+  const int K = mu * Im;
+
+  for (int a = wave; a < n_act; a += 4) {
+    const int e = active[a];
+    const int seg = offsets[e], n = offsets[e + 1] - seg;
+    const bool row_ok = fr < n;
+    const uint16_t* arow = h + (size_t)(seg + min(fr, n - 1)) * K + fk;
+    const uint16_t* brow = w2 + ((size_t)e * H + n0 + fr) * Im + fk;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < K; k0 += 32 * kUnroll) {
+      uint4 av[kUnroll], bv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int kg = k0 + 32 * u;
+        const int mm = kg / Im;
+        bv[u] = *reinterpret_cast<const uint4*>(brow + (size_t)mm * E * H * Im + (kg - mm * Im));
+        av[u] = *reinterpret_cast<const uint4*>(arow + kg);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        uint4 aa = av[u];
+        if (!row_ok) aa = make_uint4(0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
+                                                      __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * (lane >> 4) + r;
+      if (row < n) {
+        const int route = perm[seg + row];  // = t * k + j
+        slot[route][fr] = topw[route] * acc[r];
+      }
+    }
+  }
+  __syncthreads();
+  // out[t, n0 + c] = sum over j ascending of the route slots
+  for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
+    const int t = i >> 4, c = i & 15;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s += slot[t * k + j][c];
+    out[(size_t)t * H + n0 + c] = float_to_bf16_bits(s);
+  }
+}
+
+}  // namespace
+
+size_t decode_scratch_bytes() {
+  return (size_t)kSplit * kDecT * kMaxExperts * sizeof(double) + (kMaxExperts + 1) * sizeof(int32_t);
+}
+
+bool decode_supported(const Shape& s) {
+  return s.bf16 && s.T >= 1 && s.T <= kDecT && s.k <= kMaxK && (s.H % (kSplit * 128)) == 0 &&
+         (s.Im % 64) == 0 && (s.mu * s.Im) % 64 == 0 && (s.H % (32 * kUnroll)) == 0 &&
+         (s.Im % (32 * kUnroll)) == 0 && (s.H % 16) == 0;
+}
+
+hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const float* bias,
+                         const void* w1, const void* w2, void* out, float* logits, int32_t* ids,
+                         float* w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                         void* h, void* scratch, hipStream_t st) {
+  double* partial = (double*)scratch;
+  int32_t* active = (int32_t*)((char*)scratch + (size_t)kSplit * kDecT * kMaxExperts * sizeof(double));
+  hipLaunchKernelGGL(decode_route_partial, dim3(kSplit), dim3(256), 0, st, (const uint16_t*)x, wg,
+                     s.T, s.H, s.E, partial);
+  hipLaunchKernelGGL(decode_route_finish, dim3(1), dim3(1024), 0, st, partial, bias, s.T, s.E,
+                     s.k, logits, ids, w, counts, offsets, perm, inv, active);
+  const int ncg = s.mu * s.Im / 64;
+  hipLaunchKernelGGL(decode_w13, dim3(s.E * ncg), dim3(256), 0, st, (const uint16_t*)x, perm,
+                     offsets, active, (const uint16_t*)w1, s.H, s.E, s.k, s.Im, s.mu, ncg,
+                     (uint16_t*)h);
+  hipLaunchKernelGGL(decode_down_finalize, dim3(s.H / 16), dim3(256), 0, st, (const uint16_t*)h,
+                     perm, offsets, active, w, (const uint16_t*)w2, s.T, s.H, s.E, s.k, s.Im,
+                     s.mu, (uint16_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

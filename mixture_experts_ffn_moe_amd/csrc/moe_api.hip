@@ -68,6 +68,7 @@ void layout_of(const Shape& s, moe_workspace_layout* L) {
   L->inv = o;      o = align_up(o + R * 4);
   L->h = o;        o = align_up(o + R * (size_t)s.mu * s.Im * elem_bytes(s));
   L->y = o;        o = align_up(o + R * (size_t)s.H * elem_bytes(s));
+  L->scratch = o;  o = align_up(o + moe::decode_scratch_bytes());
   L->total = o;
 }
 
@@ -188,6 +189,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, c
   void* y = ws + L.y;
   hipStream_t st = (hipStream_t)stream;
 
+  if (moe::decode_supported(s))
+    return hip_status(moe::launch_decode(s, x, wg, bias, w1, w2, out, logits, ids, w, counts,
+                                         offsets, perm, inv, h, ws + L.scratch, st));
   MOE_CHECK(hip_status(moe::launch_route(s, x, wg, bias, logits, ids, w, st)));
   MOE_CHECK(hip_status(moe::launch_permute(s, ids, counts, offsets, perm, inv, st)));
   MOE_CHECK(hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, st)));

@@ -71,4 +71,12 @@ hipError_t launch_down(const Shape& s, const void* h, const int32_t* offsets, co
 hipError_t launch_finalize(const Shape& s, const void* y, const int32_t* inv, const float* w,
                            void* out, hipStream_t st);
 
+// Small-token path (decode.hip).
+size_t decode_scratch_bytes();
+bool decode_supported(const Shape& s);
+hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const float* bias,
+                         const void* w1, const void* w2, void* out, float* logits, int32_t* ids,
+                         float* w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                         void* h, void* scratch, hipStream_t st);
+
 }  // namespace moe

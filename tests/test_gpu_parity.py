@@ -302,3 +302,47 @@ def test_micro_views_sum_to_multi_micro(m):
     assert_close(full, ref, mi.BF16, "2-micro")
     ma, rl = errors(parts[0] + parts[1], full)
     assert ma <= 2 * TOL[mi.BF16][0] and rl <= 2 * TOL[mi.BF16][1], (ma, rl)
+
+
+# ------------------------------------------------------------------ small-token (decode) path
+
+DECODE = [
+    dict(T=1, H=2048, E=8, k=2, Im=256, micro=1, seed=31),
+    dict(T=3, H=2048, E=64, k=8, Im=256, micro=2, seed=32),
+    dict(T=8, H=2048, E=16, k=16, Im=512, micro=1, seed=33),
+    dict(T=16, H=4096, E=64, k=8, Im=256, micro=1, seed=34),
+    dict(T=16, H=2048, E=32, k=4, Im=256, micro=2, seed=35, zipf={"s": 1.2, "scale": 6.0, "seed": 35}),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[f"T{c['T']}_E{c['E']}_k{c['k']}_mu{c['micro']}" for c in DECODE])
+def test_decode_path(m, case):
+    """moe_forward with T <= 16 takes the weight-streaming path: routing and h
+    are the same bits as the step-wise path, the output meets the bar
+    against the oracle (every element) and against the step-wise path."""
+    c = dict(case)
+    zipf = c.pop("zipf", None)
+    # the workload's distributions (x ~ N(0,1), router and expert weights
+    # ~ N(0, 0.02)), on which the absolute output bar is defined
+    sp = mi.custom_spec(dtype=mi.BF16, zipf=zipf, name="decode", sigma_g=0.02, sigma_w=0.02, **c)
+    say(f"[parity] decode path T={sp.T} H={sp.H} E={sp.E} k={sp.k} Im={sp.Im} mu={sp.micro}")
+    inp = mi.make_layer(sp)
+    ref = o.forward(inp)
+    d = device_inputs(inp)
+    steps = run_steps(m, sp, d)
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    buf = MoELayerBuffers(shape_of(sp))
+    out = buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    v = buf.views()
+    check_routing(sp, inp, v, ref)
+    for f in ("logits", "ids", "w", "counts", "offsets", "perm", "inv", "h"):
+        assert torch.equal(v[f].view(torch.int16) if v[f].dtype == torch.bfloat16 else v[f],
+                           steps[f].view(torch.int16) if steps[f].dtype == torch.bfloat16 else steps[f]), f
+    ma, rl = assert_close(to_host_f32(out), ref["out"], sp.dtype, "decode out")
+    e2 = errors(to_host_f32(out), to_host_f32(steps["out"]))
+    assert e2[0] <= 2 * TOL[mi.BF16][0] and e2[1] <= 2 * TOL[mi.BF16][1], e2
+    out2 = MoELayerBuffers(shape_of(sp)).forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    say(f"[parity] decode: out max-abs {ma:.2e} rel-L2 {rl:.2e}")
