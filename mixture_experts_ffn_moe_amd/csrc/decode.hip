@@ -96,23 +96,38 @@ __global__ __launch_bounds__(256) void decode_route_partial(const uint16_t* __re
   f64x4 acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int c = 0; c < hq; c += 32) {
-    float xv[8], wv[4][8];
-    load8f(xrow + c, xv);
+  float xv[2][8], wv[2][4][8];
+  auto load_chunk = [&](int c, int b) {
+    load8f(xrow + c, xv[b]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 a = *reinterpret_cast<const float4*>(wrow[q] + c);
-      const float4 b = *reinterpret_cast<const float4*>(wrow[q] + c + 4);
-      wv[q][0] = a.x; wv[q][1] = a.y; wv[q][2] = a.z; wv[q][3] = a.w;
-      wv[q][4] = b.x; wv[q][5] = b.y; wv[q][6] = b.z; wv[q][7] = b.w;
+      const float4 bb = *reinterpret_cast<const float4*>(wrow[q] + c + 4);
+      wv[b][q][0] = a.x; wv[b][q][1] = a.y; wv[b][q][2] = a.z; wv[b][q][3] = a.w;
+      wv[b][q][4] = bb.x; wv[b][q][5] = bb.y; wv[b][q][6] = bb.z; wv[b][q][7] = bb.w;
     }
+  };
+  auto mma_chunk = [&](int b) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const double a = tok_ok ? (double)xv[m] : 0.0;
+      const double a = tok_ok ? (double)xv[b][m] : 0.0;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[q][m] : 0.0, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[b][q][m] : 0.0, acc[q], 0, 0, 0);
     }
+  };
+  // hq = H / 64 is a multiple of 32: pairs of chunks (the second in flight
+  // while the first is consumed), then one trailing chunk when hq % 64 == 32
+  int c = 0;
+  for (; c + 64 <= hq; c += 64) {
+    load_chunk(c, 0);
+    load_chunk(c + 32, 1);
+    mma_chunk(0);
+    mma_chunk(1);
+  }
+  if (c < hq) {
+    load_chunk(c, 0);
+    mma_chunk(0);
   }
   // fp64 16x16 D layout: register r holds row (lane/16) + 4r, column lane%16
 #pragma unroll

@@ -130,10 +130,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 
 // bf16 tile configurations (measured on MI355X for the denoise layer):
 // w13: 256 rows x (128 gate + 128 up) B-rows, BK 64, 2 stages, 8 waves of
-// 128 x 64; down: 256 x 256, BK 32, 4 stages, 8 waves.  Two waves per SIMD
+// 128 x 64; down: the same shape with 256 output columns.  BK 64 keeps every
+// row copy a full 128-byte line (64-byte pieces halve the copy rate).  Two waves per SIMD
 // are needed for the matrix pipe to issue at full rate.
 using W13Cfg = fast::Cfg<fast::kW13, 256, 256, 64, 2, 2, 4>;
-using DownCfg = fast::Cfg<fast::kDown, 256, 256, 32, 4, 2, 4>;
+using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4>;
 
 
 inline unsigned grid_size(long long tiles) {

@@ -110,18 +110,29 @@ __global__ __launch_bounds__(256) void route_kernel(const XT* __restrict__ x,
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  for (int c = 0; c < hq; c += 32) {
-    float xv[8], wv[4][8];
-    load8(xrow + c, xv);
+  // chunk loads are double-buffered: chunk c+32 is in flight while the
+  // 32 MFMAs of chunk c run (hq is a multiple of 64)
+  float xv[2][8], wv[2][4][8];
+  auto load_chunk = [&](int c, int b) {
+    load8(xrow + c, xv[b]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load8(wrow[q] + c, wv[q]);
+    for (int q = 0; q < 4; ++q) load8(wrow[q] + c, wv[b][q]);
+  };
+  auto mma_chunk = [&](int b) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const double a = tok_ok ? (double)xv[m] : 0.0;
+      const double a = tok_ok ? (double)xv[b][m] : 0.0;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[q][m] : 0.0, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[b][q][m] : 0.0, acc[q], 0, 0, 0);
     }
+  };
+  load_chunk(0, 0);
+  for (int c = 0; c < hq; c += 64) {
+    load_chunk(c + 32, 1);
+    mma_chunk(0);
+    if (c + 64 < hq) load_chunk(c + 64, 0);
+    mma_chunk(1);
   }
   // fp64 16x16 D layout: register r of lane holds row (lane/16) + 4r (token),
   // column lane%16 (expert)
