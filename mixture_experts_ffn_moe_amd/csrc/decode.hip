@@ -18,8 +18,8 @@
 //      micro-major intermediate); each wave streams 16 gate and 16 up rows of
 //      w1 straight from memory into MFMA B fragments (M = the expert's rows,
 //      padded to 16) and applies SwiGLU; h is rounded to bf16.
-//   4. decode_down_finalize: one workgroup per 16 output columns; its waves
-//      split the active experts, stream the matching w2 rows, and put
+//   4. decode_down_finalize: one workgroup per 16 output columns; its eight
+//      waves split the active experts (enough loads in flight per CU), stream the matching w2 rows, and put
 //      w[t, j] * y[route (t, j)] into a per-route LDS slot; the slots are then
 //      summed in ascending j (the finalize of section 6.1), so the down
 //      partials of every micro-shard and route are reduced once, without
@@ -231,7 +231,8 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
 
 // ---------------------------------------------------------------------------
 // 3. gate|up + SwiGLU for one active expert and 64 intermediate columns.
-constexpr int kUnroll = 8;  // k-steps of 32 in flight per wave
+constexpr int kUnroll = 8;     // k-steps of 32 in flight per wave
+constexpr int kDownWaves = 8;  // waves of the down+finalize workgroup (they split the experts)
 
 __global__ __launch_bounds__(256) void decode_w13(const uint16_t* __restrict__ x,
                                                   const int32_t* __restrict__ perm,
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(256) void decode_w13(const uint16_t* __restrict__ x
 
 // ---------------------------------------------------------------------------
 // 4. down projection + finalize for 16 output columns and all tokens.
-__global__ __launch_bounds__(256) void decode_down_finalize(
+__global__ __launch_bounds__(kDownWaves * 64) void decode_down_finalize(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const float* __restrict__ topw, const uint16_t* __restrict__ w2, int T, int H, int E, int k,
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(256) void decode_down_finalize(
   const int n_act = active[kMaxExperts];
   const int K = mu * Im;
 
-  for (int a = wave; a < n_act; a += 4) {
+  for (int a = wave; a < n_act; a += kDownWaves) {
     const int e = active[a];
     const int seg = offsets[e], n = offsets[e + 1] - seg;
     const bool row_ok = fr < n;
@@ -366,7 +367,7 @@ hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const f
   hipLaunchKernelGGL(decode_w13, dim3(s.E * ncg), dim3(256), 0, st, (const uint16_t*)x, perm,
                      offsets, active, (const uint16_t*)w1, s.H, s.E, s.k, s.Im, s.mu, ncg,
                      (uint16_t*)h);
-  hipLaunchKernelGGL(decode_down_finalize, dim3(s.H / 16), dim3(256), 0, st, (const uint16_t*)h,
+  hipLaunchKernelGGL(decode_down_finalize, dim3(s.H / 16), dim3(kDownWaves * 64), 0, st, (const uint16_t*)h,
                      perm, offsets, active, w, (const uint16_t*)w2, s.T, s.H, s.E, s.k, s.Im,
                      s.mu, (uint16_t*)out);
   return hipGetLastError();
