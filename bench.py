@@ -9,7 +9,9 @@ roofline position measured with HIP events, the other workload layers
 (2-micro denoise, AR decode in GB/s, skewed CFG batch) and the CPU oracle's
 rate on a bounded sample of the same layer.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-extra] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 20] [--no-extra] [--no-cpu]
+    python bench.py --copy-calibration     # 1 GiB device copy, for counter scaling
+    python bench.py --only-decode          # the AR-decode layer alone, for profiling
 """
 from __future__ import annotations
 
@@ -29,6 +31,15 @@ import moe_inputs as mi  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# Sources of the w13 grouped GEMM kernel, and the rocprofv3 counter summary of
+# its HBM traffic.  The summary records the sha256 of these sources at the
+# time the counters were taken; the traffic is reported only while it matches.
+W13_KERNEL_SOURCES = ("mixture_experts_ffn_moe_amd/csrc/gemm_fast.h",
+                      "mixture_experts_ffn_moe_amd/csrc/gemm.hip",
+                      "mixture_experts_ffn_moe_amd/csrc/moe_common.h")
+W13_TRAFFIC_PROFILE = "profiles/w13_swiglu_gemm_denoise_traffic.md"
+COPY_CALIBRATION_BYTES = 1 << 30
 METRIC = "MoE layer TFLOP/s + tokens/s (T=4096, 64E top-8 bf16); decode GB/s; % roofline"
 
 
@@ -47,6 +58,60 @@ def decode_bytes(sp, n_active: int) -> int:
     down weights once, x and out once, the router weights once."""
     per_expert = (2 * sp.I * sp.H + sp.H * sp.I) * 2
     return n_active * per_expert + sp.T * sp.H * 2 * 2 + sp.E * sp.H * 4
+
+
+def w13_algorithmic_bytes(sp) -> int:
+    """HBM bytes the w13 GEMM must move at least: every expert's gate|up
+    weights and x once, h written once, the permutation and offsets."""
+    R = sp.T * sp.k
+    return (sp.micro * sp.E * 2 * sp.Im * sp.H + sp.T * sp.H + R * sp.I) * 2 + R * 4 + (sp.E + 1) * 4
+
+
+def kernel_sources_sha256(paths=W13_KERNEL_SOURCES) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path=W13_TRAFFIC_PROFILE):
+    """HBM bytes per launch of the w13 kernel from the committed counter
+    summary (`key: value` lines), or None if it is missing or was taken on
+    other kernel sources."""
+    full = os.path.join(ROOT, path)
+    if not os.path.exists(full):
+        return None
+    kv = {}
+    with open(full) as f:
+        for line in f:
+            if ":" in line and line.split(":", 1)[0].strip() in (
+                    "kernel_sources_sha256", "fetch_bytes_per_launch", "write_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        fetch, write = int(kv["fetch_bytes_per_launch"]), int(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+    return {"read": fetch, "write": write, "total": fetch + write}
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    byte counters (FETCH_SIZE, WRITE_SIZE) of the kernels above."""
+    n = COPY_CALIBRATION_BYTES
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                                           "launches": 3, "kernel": "__amd_rocclr_copyBuffer"}}),
+          flush=True)
+    return 0
 
 
 def dev(a, torch):
@@ -133,6 +198,18 @@ def time_kernels(moe, torch, d, steps, warmup):
     return res, cnt.cpu().numpy()
 
 
+def time_decode(moe, torch, steps, warmup):
+    """The AR-decode layer (T=8): moe_forward time and algorithmic GB/s."""
+    sp3 = mi.spec(3)
+    d3 = upload(mi.make_layer(sp3), torch)
+    ms3, _, b3 = time_forward(moe, torch, d3, steps, warmup)
+    n_active = int((b3.views()["counts"].cpu().numpy() > 0).sum())
+    gbs = decode_bytes(sp3, n_active) / (ms3 * 1e-3) / 1e9
+    return {"ms": round(ms3, 5), "GB_per_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "active_experts": n_active,
+            "algorithmic_bytes": decode_bytes(sp3, n_active)}
+
+
 def cpu_baseline(base, n_tokens: int):
     """The oracle as it stands, on the first n_tokens tokens of the layer."""
     import dataclasses
@@ -161,10 +238,14 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the decode, 2-micro and skewed layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="only time the AR-decode layer (for profiling) and print its numbers")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -177,6 +258,14 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+
+    if args.copy_calibration:
+        return copy_calibration(torch)
+    if args.only_decode:
+        dec = time_decode(moe, torch, max(args.steps, 50), args.warmup)
+        log(f"decode {dec['ms'] * 1e3:.1f} us, {dec['GB_per_s']:.0f} GB/s")
+        print(json.dumps({"decode": dec}), flush=True)
+        return 0
 
     sp = mi.spec(1)
     log(f"generating {sp.name}")
@@ -193,6 +282,7 @@ def main(argv=None):
     w13_ms = kern["w13_swiglu"]
     achieved = w13_flops(sp) / (w13_ms * 1e-3) / 1e12
     down_tf = 2.0 * sp.T * sp.k * sp.I * sp.H / (kern["down"] * 1e-3) / 1e12
+    traffic = measured_traffic()
 
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
@@ -206,9 +296,12 @@ def main(argv=None):
                                "down [64,4096,1536])",
                    "T": sp.T, "H": sp.H, "E": sp.E, "k": sp.k, "I": sp.I, "micro_count": sp.micro,
                    "parallelism": "single GPU (one TP2 rank's shard)"},
-        "roofline": {"kernel": "grouped_gemm_bf16<w13> (gate|up GEMM + SwiGLU)", "bound": "mfma",
+        "roofline": {"kernel": "grouped_gemm<w13> (gathered gate|up GEMM + SwiGLU)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else traffic["total"],
+                     "traffic_read_write": traffic,
+                     "algorithmic_bytes_per_launch": w13_algorithmic_bytes(sp),
                      "avg_launch_ms": round(w13_ms, 5),
                      "algorithmic_flops_per_launch": w13_flops(sp)},
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
@@ -246,15 +339,9 @@ def main(argv=None):
         del d2, d4, b4buf
         torch.cuda.empty_cache()
         # AR decode
-        sp3 = mi.spec(3)
-        d3 = upload(mi.make_layer(sp3), torch)
-        ms3, _, b3 = time_forward(moe, torch, d3, max(args.steps, 50), args.warmup)
-        n_active = int((b3.views()["counts"].cpu().numpy() > 0).sum())
-        gbs = decode_bytes(sp3, n_active) / (ms3 * 1e-3) / 1e9
-        extra["decode"] = {"ms": round(ms3, 5), "GB_per_s": round(gbs, 1),
-                           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "active_experts": n_active,
-                           "algorithmic_bytes": decode_bytes(sp3, n_active)}
-        log(f"decode {ms3 * 1e3:.1f} us, {gbs:.0f} GB/s, {n_active} active experts")
+        extra["decode"] = time_decode(moe, torch, max(args.steps, 50), args.warmup)
+        log(f"decode {extra['decode']['ms'] * 1e3:.1f} us, {extra['decode']['GB_per_s']:.0f} GB/s, "
+            f"{extra['decode']['active_experts']} active experts")
         res["other_layers"] = extra
 
     if not args.no_cpu:
