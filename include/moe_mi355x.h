@@ -76,7 +76,8 @@ typedef struct {
   size_t inv;      /* int32   [R]            */
   size_t h;        /* dtype   [R, mu*Im]     */
   size_t y;        /* dtype   [R, H]         */
-  size_t scratch;  /* small-token path: fp64 router partials and the active-expert list */
+  size_t scratch;  /* token path: int32 [ceil(T/16), 64] expert counts per 16-token router
+                      block; small-token path: fp64 router partials, active-expert list */
   size_t total;    /* bytes needed            */
 } moe_workspace_layout;
 

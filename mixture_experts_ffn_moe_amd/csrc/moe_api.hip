@@ -6,6 +6,8 @@
 #include "../../include/moe_mi355x.h"
 #include "moe_common.h"
 
+#include <algorithm>
+
 using moe::Shape;
 
 namespace {
@@ -68,7 +70,8 @@ void layout_of(const Shape& s, moe_workspace_layout* L) {
   L->inv = o;      o = align_up(o + R * 4);
   L->h = o;        o = align_up(o + R * (size_t)s.mu * s.Im * elem_bytes(s));
   L->y = o;        o = align_up(o + R * (size_t)s.H * elem_bytes(s));
-  L->scratch = o;  o = align_up(o + moe::decode_scratch_bytes());
+  L->scratch = o;
+  o = align_up(o + std::max(moe::decode_scratch_bytes(), moe::route_hist_bytes(s)));
   L->total = o;
 }
 
@@ -192,8 +195,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, c
   if (moe::decode_supported(s))
     return hip_status(moe::launch_decode(s, x, wg, bias, w1, w2, out, logits, ids, w, counts,
                                          offsets, perm, inv, h, ws + L.scratch, st));
-  MOE_CHECK(hip_status(moe::launch_route(s, x, wg, bias, logits, ids, w, st)));
-  MOE_CHECK(hip_status(moe::launch_permute(s, ids, counts, offsets, perm, inv, st)));
+  int32_t* hist = (int32_t*)(ws + L.scratch);
+  MOE_CHECK(hip_status(moe::launch_route(s, x, wg, bias, logits, ids, w, st, hist)));
+  MOE_CHECK(hip_status(moe::launch_permute_hist(s, ids, hist, counts, offsets, perm, inv, st)));
   MOE_CHECK(hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, st)));
   MOE_CHECK(hip_status(moe::launch_down(s, h, offsets, w2, y, st)));
   MOE_CHECK(hip_status(moe::launch_finalize(s, y, inv, w, out, st)));

@@ -53,11 +53,25 @@ struct Shape {
   long long R() const { return (long long)T * k; }
 };
 
+// Tokens per router workgroup; with a non-null `hist` the router also writes
+// hist[b][e] (int32, kMaxExperts per row) = routes of tokens
+// [kRouteTokTile*b, kRouteTokTile*(b+1)) that went to expert e.
+constexpr int kRouteTokTile = 16;
+inline size_t route_hist_bytes(const Shape& s) {
+  return (size_t)((s.T + kRouteTokTile - 1) / kRouteTokTile) * kMaxExperts * 4;
+}
+
 hipError_t launch_route(const Shape& s, const void* x, const float* wg, const float* bias,
-                        float* logits, int32_t* ids, float* w, hipStream_t st);
+                        float* logits, int32_t* ids, float* w, hipStream_t st,
+                        int32_t* hist = nullptr);
 
 hipError_t launch_permute(const Shape& s, const int32_t* ids, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t st);
+
+// Same outputs as launch_permute from the router's per-block histograms.
+hipError_t launch_permute_hist(const Shape& s, const int32_t* ids, const int32_t* hist,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                               hipStream_t st);
 
 hipError_t launch_gather(const Shape& s, const void* x, const int32_t* perm, void* xp,
                          hipStream_t st);

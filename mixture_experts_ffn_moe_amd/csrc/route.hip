@@ -12,15 +12,15 @@
 //
 // One workgroup handles kTokTile tokens: the fp64 logit tile [kTokTile x 64]
 // is accumulated on the fp64 matrix pipe, then each wave runs the top-k of
-// its tokens with one lane per expert: k rounds of a 64-lane arg-max over the
-// key (orderable(logit) << 32 | (63 - e)), so equal logits go to the lower
-// expert index.
+// its tokens with one lane per expert: k rounds of a 64-lane maximum of the
+// orderable logit key, the winner being the lowest lane that holds it, so
+// equal logits go to the lower expert index.
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTokTile = 16;  // tokens per workgroup
+constexpr int kTokTile = kRouteTokTile;  // tokens per workgroup
 
 // Orderable 32-bit key of a float: unsigned order equals numeric order and
 // -0.0 maps to the key of +0.0.
@@ -34,15 +34,23 @@ __device__ __forceinline__ float from_orderable(uint32_t k) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, d);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// Maximum of v over the 64 lanes, returned to every lane.  DPP row shifts
+// build the maximum of each 16-lane row in its lane 15, row broadcasts carry
+// it into lane 63; a lane whose DPP source is out of range or masked keeps its
+// own value (old = v), which max leaves unchanged.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xf, false);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -72,79 +80,93 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 }
 
 // Logit tile of kTokTile tokens x 64 experts on the fp64 matrix pipe
-// (v_mfma_f64_16x16x4_f64, exact products, fp64 sums).  Wave w covers the
-// hidden range [w*H/4, (w+1)*H/4) for all four 16-expert tiles; lane
-// (t = lane%16, g = lane/16) holds x[t][h0 + 8g + m] and wg[16q + t][h0 + 8g + m]
-// as the m-th MFMA's A and B elements, so the 8 MFMAs of a 32-wide chunk sum
-// every h of the chunk exactly once.  The four wave partials are added in a
-// fixed order, so the logits are reproducible run to run.
+// (v_mfma_f64_16x16x4_f64, exact products, fp64 sums).  Eight waves, two per
+// SIMD (a single wave cannot keep the matrix pipe busy): wave w covers the
+// hidden quarter hw = w%4, [hw*H/4, (hw+1)*H/4), for the 16-expert tiles
+// q = 2*(w/4) and 2*(w/4)+1; lane (t = lane%16, g = lane/16) holds
+// x[t][h0 + 8g + m] and wg[16q + t][h0 + 8g + m] as the m-th MFMA's A and B
+// elements, so the 8 MFMAs of a 32-wide chunk sum every h of the chunk
+// exactly once.  The four quarter partials are added in a fixed order, so the
+// logits are reproducible run to run.
+constexpr int kRouteWaves = 8;
+
 template <typename XT>
-__global__ __launch_bounds__(256) void route_kernel(const XT* __restrict__ x,
+__global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __restrict__ x,
                                                     const float* __restrict__ wg,
                                                     const float* __restrict__ bias, int T, int H,
                                                     int E, int k, float* __restrict__ logits,
                                                     int32_t* __restrict__ ids,
-                                                    float* __restrict__ topw) {
+                                                    float* __restrict__ topw,
+                                                    int32_t* __restrict__ hist) {
   __shared__ double part[4][kTokTile][kMaxExperts + 1];
   __shared__ float lg[kTokTile][kMaxExperts];
+  __shared__ int hcnt[kMaxExperts];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int hw = wave & 3, eh = wave >> 2;  // hidden quarter, expert half
   const int t0 = blockIdx.x * kTokTile;
   const int tl = lane & 15, g = lane >> 4;
   const int hq = H / 4;
-  const int hb = wave * hq;
+  const int hb = hw * hq;
 
-  const bool tok_ok = t0 + tl < T;
+  if (tid < kMaxExperts) hcnt[tid] = 0;  // ordered before its use by the barriers below
+
+  // rows past T and experts past E read the last valid row instead: their
+  // logits are computed but never stored or ranked, so no operand is masked
   const XT* xrow = x + (size_t)min(t0 + tl, T - 1) * H + hb + 8 * g;
-  const float* wrow[4];
-  bool w_ok[4];
+  const float* wrow[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = 16 * q + tl;
-    w_ok[q] = e < E;
+  for (int q = 0; q < 2; ++q) {
+    const int e = 16 * (2 * eh + q) + tl;
     wrow[q] = wg + (size_t)min(e, E - 1) * H + hb + 8 * g;
   }
 
-  f64x4 acc[4];
+  f64x4 acc[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int q = 0; q < 2; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // chunk loads are double-buffered: chunk c+32 is in flight while the
-  // 32 MFMAs of chunk c run (hq is a multiple of 64)
-  float xv[2][8], wv[2][4][8];
+  // 16 MFMAs of chunk c run (hq is a multiple of 64)
+  float xv[2][8], wv[2][2][8];
   auto load_chunk = [&](int c, int b) {
     load8(xrow + c, xv[b]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load8(wrow[q] + c, wv[b][q]);
+    for (int q = 0; q < 2; ++q) load8(wrow[q] + c, wv[b][q]);
   };
   auto mma_chunk = [&](int b) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const double a = tok_ok ? (double)xv[b][m] : 0.0;
+      const double a = (double)xv[b][m];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[b][q][m] : 0.0, acc[q], 0, 0, 0);
+      for (int q = 0; q < 2; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)wv[b][q][m], acc[q], 0, 0, 0);
     }
   };
+  // the scheduling barriers keep each prefetch ahead of the MFMAs it is
+  // meant to overlap (left alone, the compiler sinks the loads to their use)
   load_chunk(0, 0);
   for (int c = 0; c < hq; c += 64) {
     load_chunk(c + 32, 1);
+    __builtin_amdgcn_sched_barrier(0);
     mma_chunk(0);
+    __builtin_amdgcn_sched_barrier(0);
     if (c + 64 < hq) load_chunk(c + 64, 0);
+    __builtin_amdgcn_sched_barrier(0);
     mma_chunk(1);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // fp64 16x16 D layout: register r of lane holds row (lane/16) + 4r (token),
   // column lane%16 (expert)
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[wave][g + 4 * r][16 * q + tl] = acc[q][r];
+    for (int r = 0; r < 4; ++r) part[hw][g + 4 * r][16 * (2 * eh + q) + tl] = acc[q][r];
   __syncthreads();
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
+  for (int i = 0; i < kTokTile * kMaxExperts / (kRouteWaves * 64); ++i) {
+    const int idx = tid + kRouteWaves * 64 * i;
     const int r = idx >> 6, e = idx & 63;
     const double s = ((part[0][r][e] + part[1][r][e]) + part[2][r][e]) + part[3][r][e];
     const double b = (bias != nullptr && e < E) ? (double)bias[e] : 0.0;
@@ -154,22 +176,28 @@ __global__ __launch_bounds__(256) void route_kernel(const XT* __restrict__ x,
   }
   __syncthreads();
 
-  // top-k: wave w handles tokens w*4 .. w*4+3, lane = expert.
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 4 + i, t = t0 + r;
+  // top-k: wave w handles tokens w*2 and w*2+1, lane = expert.
+  constexpr int kTokPerWave = kTokTile / kRouteWaves;
+  for (int i = 0; i < kTokPerWave; ++i) {
+    const int r = wave * kTokPerWave + i, t = t0 + r;
     if (t >= T) break;
-    uint64_t key = 0;
-    if (lane < E) key = ((uint64_t)orderable(lg[r][lane]) << 32) | (uint32_t)(63 - lane);
+    // key 0 is below every finite logit's key: it marks lanes past E and
+    // experts already taken
+    uint32_t key = lane < E ? orderable(lg[r][lane]) : 0u;
     float mine = 0.0f;    // lane j keeps the j-th selected logit
     float first = 0.0f;   // the largest logit
     for (int j = 0; j < k; ++j) {
-      const uint64_t m = wave_max_u64(key);
-      const int win = 63 - (int)(m & 0xffffffffu);
-      const float Lw = from_orderable((uint32_t)(m >> 32));
+      const uint32_t m = wave_max_u32(key);
+      // the lowest lane holding the maximum: equal logits go to the lower expert
+      const int win = __ffsll((long long)__ballot(key == m)) - 1;
+      const float Lw = from_orderable(m);
       if (j == 0) first = Lw;
       if (lane == j) mine = Lw;
       if (lane == win) key = 0;
-      if (lane == 0) ids[(size_t)t * k + j] = win;
+      if (lane == 0) {
+        ids[(size_t)t * k + j] = win;
+        if (hist != nullptr) atomicAdd(&hcnt[win], 1);
+      }
     }
     // weights: softmax restricted to the selected experts (the full softmax
     // denominator cancels in the renormalisation), in fp64.
@@ -177,19 +205,24 @@ __global__ __launch_bounds__(256) void route_kernel(const XT* __restrict__ x,
     const double s = wave_sum_f64(ex);
     if (lane < k) topw[(size_t)t * k + lane] = (float)(ex / s);
   }
+  if (hist != nullptr) {
+    __syncthreads();
+    if (tid < kMaxExperts) hist[(size_t)blockIdx.x * kMaxExperts + tid] = hcnt[tid];
+  }
 }
 
 }  // namespace
 
 hipError_t launch_route(const Shape& s, const void* x, const float* wg, const float* bias,
-                        float* logits, int32_t* ids, float* w, hipStream_t st) {
+                        float* logits, int32_t* ids, float* w, hipStream_t st, int32_t* hist) {
   const int blocks = (s.T + kTokTile - 1) / kTokTile;
+  const dim3 block(kRouteWaves * 64);
   if (s.bf16)
-    hipLaunchKernelGGL(route_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
-                       (const uint16_t*)x, wg, bias, s.T, s.H, s.E, s.k, logits, ids, w);
+    hipLaunchKernelGGL(route_kernel<uint16_t>, dim3(blocks), block, 0, st,
+                       (const uint16_t*)x, wg, bias, s.T, s.H, s.E, s.k, logits, ids, w, hist);
   else
-    hipLaunchKernelGGL(route_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float*)x, wg,
-                       bias, s.T, s.H, s.E, s.k, logits, ids, w);
+    hipLaunchKernelGGL(route_kernel<float>, dim3(blocks), block, 0, st, (const float*)x, wg,
+                       bias, s.T, s.H, s.E, s.k, logits, ids, w, hist);
   return hipGetLastError();
 }
 
