@@ -229,8 +229,9 @@ def cpu_baseline(base, n_tokens: int):
         "value": round(expert_flops(sp) / dt / 1e12, 6), "unit": "TFLOP/s",
         "tokens_per_s": round(n_tokens / dt, 2), "seconds": round(dt, 2), "cores": int(threads),
         "kind": "oracle",
-        "sample": f"oracle forward (fp64 numpy, full routing + all {sp.E} experts) on the first "
-                  f"{n_tokens} of {base.spec.T} tokens of the same layer",
+        "sample": (f"oracle forward (fp64 numpy, full routing + all {sp.E} experts) on "
+                   + (f"the whole layer ({n_tokens} tokens)" if n_tokens >= base.spec.T else
+                      f"the first {n_tokens} of {base.spec.T} tokens of the same layer")),
     }
 
 
