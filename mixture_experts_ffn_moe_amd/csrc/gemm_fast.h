@@ -356,7 +356,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
           for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
         }
       } else if (nf > 0) {
 #pragma unroll
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
               const bf16x8 af = *reinterpret_cast<const bf16x8*>(s + fa[i] + ch);
 #pragma unroll
               for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af, acc[i][j], 0, 0, 0);
             }
           }
         }
@@ -383,26 +383,28 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
   else
     kloop(BoolTag<false>{});
 
-  // ---- epilogue: lane holds rows 4*(lane>>4)+r, column lane&15 of each block
+  // ---- epilogue.  The weights are the MFMA's first operand, so in block
+  // (i, j) lane holds token row 16*i + lane%16 and the four consecutive
+  // output columns 16*j + 4*(lane/16) + r, r = 0..3: one 8-byte store each.
   const int ldc = (C::MODE == kW13) ? mu * Im : H;
+  const int cq = 4 * (lane >> 4);
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
+    const int p = ti.m0 + wm * C::TM + 16 * i + (lane & 15);
+    if (p >= ti.seg_end) continue;
+    uint16_t* crow = Cout + (size_t)p * ldc;
+    if (C::MODE == kW13) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = ti.m0 + wm * C::TM + 16 * i + 4 * (lane >> 4) + r;
-      if (p >= ti.seg_end) continue;
-      uint16_t* crow = Cout + (size_t)p * ldc;
-      if (C::MODE == kW13) {
+      for (int j = 0; j < C::FN / 2; ++j) {
+        f32x4 v;
 #pragma unroll
-        for (int j = 0; j < C::FN / 2; ++j) {
-          const float g = acc[i][j][r], u = acc[i][j + C::FN / 2][r];
-          crow[micro * Im + n0 + wn * (C::TN / 2) + 16 * j + fr] = float_to_bf16_bits(silu_f32(g) * u);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          crow[n0 + wn * C::TN + 16 * j + fr] = float_to_bf16_bits(acc[i][j][r]);
+        for (int r = 0; r < 4; ++r) v[r] = silu_f32(acc[i][j][r]) * acc[i][j + C::FN / 2][r];
+        *reinterpret_cast<uint2*>(crow + micro * Im + n0 + wn * (C::TN / 2) + 16 * j + cq) = pack_bf16x4(v);
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        *reinterpret_cast<uint2*>(crow + n0 + wn * C::TN + 16 * j + cq) = pack_bf16x4(acc[i][j]);
     }
   }
 }
