@@ -35,25 +35,6 @@ constexpr int kMaxK = 64;
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t orderable(float f) {
-  if (f == 0.0f) f = 0.0f;
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float from_orderable(uint32_t k) {
-  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-  return __uint_as_float(u);
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, d);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d);
@@ -83,14 +64,13 @@ __global__ __launch_bounds__(256) void decode_route_partial(const uint16_t* __re
   const int tl = lane & 15, g = lane >> 4;
   const int hs = H / kSplit, hq = hs / 4;
   const int hb = blockIdx.x * hs + wave * hq;
-  const bool tok_ok = tl < T;
+  // tokens past T and experts past E read the last valid row: their partials
+  // are never used, so no operand is masked
   const uint16_t* xrow = x + (size_t)min(tl, T - 1) * H + hb + 8 * g;
   const float* wrow[4];
-  bool w_ok[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = 16 * q + tl;
-    w_ok[q] = e < E;
     wrow[q] = wg + (size_t)min(e, E - 1) * H + hb + 8 * g;
   }
   f64x4 acc[4];
@@ -110,10 +90,10 @@ __global__ __launch_bounds__(256) void decode_route_partial(const uint16_t* __re
   auto mma_chunk = [&](int b) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const double a = tok_ok ? (double)xv[b][m] : 0.0;
+      const double a = (double)xv[b][m];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, w_ok[q] ? (double)wv[b][q][m] : 0.0, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)wv[b][q][m], acc[q], 0, 0, 0);
     }
   };
   // hq = H / 64 is a multiple of 32: pairs of chunks (the second in flight
@@ -153,7 +133,8 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
     int32_t* __restrict__ inv, int32_t* __restrict__ active) {
   __shared__ float lg[kDecT][kMaxExperts];
   __shared__ int sids[kDecT * kMaxK];
-  __shared__ int cnt[kMaxExperts], base[kMaxExperts];
+  __shared__ uint64_t sel[kDecT];  // experts chosen by each token
+  __shared__ int base[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   {  // logits: thread (r, e), partials summed in split order
@@ -167,24 +148,29 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
   }
   __syncthreads();
 
-  {  // top-k and weights: wave = token, lane = expert
+  {  // top-k and weights: wave = token, lane = expert (same rules as route.hip)
     const int t = wave;
     if (t < T) {
-      uint64_t key = 0;
-      if (lane < E) key = ((uint64_t)orderable(lg[t][lane]) << 32) | (uint32_t)(63 - lane);
+      uint32_t key = lane < E ? orderable(lg[t][lane]) : 0u;
+      bool taken = false;
       float mine = 0.0f, first = 0.0f;
       for (int j = 0; j < k; ++j) {
-        const uint64_t m = wave_max_u64(key);
-        const int win = 63 - (int)(m & 0xffffffffu);
-        const float Lw = from_orderable((uint32_t)(m >> 32));
+        const uint32_t m = wave_max_u32(key);
+        const int win = __ffsll((long long)__ballot(key == m)) - 1;
+        const float Lw = from_orderable(m);
         if (j == 0) first = Lw;
         if (lane == j) mine = Lw;
-        if (lane == win) key = 0;
+        if (lane == win) {
+          key = 0;
+          taken = true;
+        }
         if (lane == 0) {
           ids[(size_t)t * k + j] = win;
           sids[t * k + j] = win;
         }
       }
+      const uint64_t chosen = __ballot(taken);
+      if (lane == 0) sel[t] = chosen;
       const double ex = (lane < k) ? exp((double)mine - (double)first) : 0.0;
       const double s = wave_sum_f64(ex);
       if (lane < k) topw[(size_t)t * k + lane] = (float)(ex / s);
@@ -192,11 +178,13 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
   }
   __syncthreads();
 
-  // counts, offsets, active list (wave 0, lane = expert)
+  // counts, offsets, active list (wave 0, lane = expert): a token chooses an
+  // expert at most once, so the count is the number of tokens whose
+  // selection holds it
   const int R = T * k;
   if (wave == 0) {
     int c = 0;
-    for (int r = 0; r < R; ++r) c += (sids[r] == lane);
+    for (int t = 0; t < T; ++t) c += (int)((sel[t] >> lane) & 1ull);
     int incl = c;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -204,7 +192,6 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
       if (lane >= d) incl += v;
     }
     const int excl = incl - c;
-    cnt[lane] = c;
     base[lane] = excl;
     if (lane < E) {
       counts[lane] = c;
@@ -218,11 +205,12 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
     if (lane == 0) active[kMaxExperts] = __popcll(act);
   }
   __syncthreads();
-  // stable scatter: route r goes after every earlier route of its expert
+  // stable scatter: the routes of expert e before r = t*k + j are those of
+  // the earlier tokens that chose e
   for (int r = tid; r < R; r += blockDim.x) {
-    const int e = sids[r];
+    const int t = r / k, e = sids[r];
     int rank = 0;
-    for (int q = 0; q < r; ++q) rank += (sids[q] == e);
+    for (int q = 0; q < t; ++q) rank += (int)((sel[q] >> e) & 1ull);
     const int p = base[e] + rank;
     perm[p] = r;
     inv[r] = p;

@@ -43,6 +43,37 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// Orderable 32-bit key of a float: unsigned order equals numeric order and
+// -0.0 maps to the key of +0.0; every finite float's key is nonzero.
+__device__ __forceinline__ uint32_t orderable(float f) {
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Maximum of v over the 64 lanes, returned to every lane.  DPP row shifts
+// build the maximum of each 16-lane row in its lane 15, row broadcasts carry
+// it into lane 63; a lane whose DPP source is out of range or masked keeps its
+// own value (old = v), which max leaves unchanged.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xf, false);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Element loads/stores for the two supported element types.  bf16 tensors
 // are moved as raw 16-bit patterns.
 template <typename T> struct Elem;
