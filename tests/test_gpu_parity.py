@@ -96,6 +96,12 @@ SMALL = [
          zipf={"s": 1.2, "scale": 6.0, "seed": 15}),
     dict(name="one_token_all_experts", T=1, H=256, E=64, k=64, Im=128, micro=1, dtype=mi.BF16, seed=16),
     dict(name="k1_many_tokens", T=2000, H=256, E=64, k=1, Im=128, micro=1, dtype=mi.BF16, seed=17),
+    # the workload's weight scale (the bf16 bar is stated for N(0, 0.02) weights;
+    # at 0.05 and I = 384 one bf16 ulp of the output nearly fills it)
+    dict(name="h768_three_micro", T=333, H=768, E=24, k=5, Im=128, micro=3, dtype=mi.BF16, seed=18,
+         sigma_g=0.02, sigma_w=0.02),
+    dict(name="im384_three_col_tiles", T=257, H=768, E=10, k=3, Im=384, micro=1, dtype=mi.BF16,
+         seed=19, sigma_g=0.02, sigma_w=0.02),
 ]
 
 
@@ -264,6 +270,31 @@ def test_full_size_forward(m, i):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     _CACHE[f"out{i}"] = to_host_f32(out)
+    del d, buf
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("i", [1, 4])
+def test_full_size_stepwise_permute_matches_forward(m, i):
+    """moe_permute (every workgroup recounts all ids, several id tiles per
+    wave at these sizes) against the one-call layer's permutation (built
+    from the router's per-block counts): the same bits."""
+    sp = mi.spec(i)
+    say(f"[parity] full-size step-wise permute {sp.name}: R={sp.T * sp.k}")
+    inp = full_layer(i)
+    d = device_inputs(inp)
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    buf = MoELayerBuffers(shape_of(sp))
+    buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    v = buf.views()
+    s = shape_of(sp)
+    c2, o2 = torch.empty_like(v["counts"]), torch.empty_like(v["offsets"])
+    p2, i2 = torch.empty_like(v["perm"]), torch.empty_like(v["inv"])
+    m.moe_permute(s, v["ids"], c2, o2, p2, i2)
+    torch.cuda.synchronize()
+    for name, a, b in (("counts", c2, v["counts"]), ("offsets", o2, v["offsets"]),
+                       ("perm", p2, v["perm"]), ("inv", i2, v["inv"])):
+        assert torch.equal(a, b), name
     del d, buf
     torch.cuda.empty_cache()
 
