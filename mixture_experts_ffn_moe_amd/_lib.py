@@ -47,7 +47,7 @@ class MoeWorkspaceLayout(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m mixture_experts_ffn_moe_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python __graft_entry__.py build")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     S = ctypes.POINTER(MoeShape)

@@ -1,6 +1,6 @@
 """Build libmoe_mi355x.so from the HIP sources with hipcc for gfx950.
 
-    python -m mixture_experts_ffn_moe_amd.build
+    python mixture_experts_ffn_moe_amd/build.py   (or: python __graft_entry__.py build)
 
 Objects go to mixture_experts_ffn_moe_amd/_build/, the shared library next to
 this file.  Every call recompiles (it is the "does it build" check)."""
