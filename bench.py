@@ -200,7 +200,7 @@ def time_kernels(moe, torch, d, steps, warmup):
 
 def time_decode(moe, torch, steps, warmup):
     """The AR-decode layer (T=8): moe_forward time and algorithmic GB/s."""
-    sp3 = mi.spec(3)
+    sp3 = mi.spec("decode")
     d3 = upload(mi.make_layer(sp3), torch)
     ms3, _, b3 = time_forward(moe, torch, d3, steps, warmup)
     n_active = int((b3.views()["counts"].cpu().numpy() > 0).sum())
@@ -268,7 +268,7 @@ def main(argv=None):
         print(json.dumps({"decode": dec}), flush=True)
         return 0
 
-    sp = mi.spec(1)
+    sp = mi.spec("denoise_1micro")
     log(f"generating {sp.name}")
     base = mi.make_layer(sp)
     d = upload(base, torch)
@@ -314,7 +314,7 @@ def main(argv=None):
     if not args.no_extra:
         extra = {}
         # 2-micro denoise (same weights, micro-major)
-        sp2 = mi.spec(2)
+        sp2 = mi.spec("denoise_2micro")
         w1, w2 = relayout_two_micro(base, sp2)
         del d
         torch.cuda.empty_cache()
@@ -326,7 +326,7 @@ def main(argv=None):
         log(f"2-micro {ms2:.4f} ms")
         del b2
         # skewed CFG batch (same 2-micro weights, T=8192, Zipf bias)
-        sp4 = mi.spec(4)
+        sp4 = mi.spec("skewed_cfg")
         wg4, bias4 = mi.make_router(sp4)
         d4 = dict(x=dev(mi.make_x(sp4), torch), wg=dev(wg4, torch), bias=dev(bias4, torch),
                   w1=d2["w1"], w2=d2["w2"], sp=sp4)

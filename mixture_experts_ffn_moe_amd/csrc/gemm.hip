@@ -129,12 +129,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 }
 
 // bf16 tile configurations (measured on MI355X for the denoise layer):
-// w13: 256 rows x (128 gate + 128 up) B-rows, BK 64, 2 stages, 8 waves of
-// 128 x 64; down: the same shape with 256 output columns.  BK 64 keeps every
-// row copy a full 128-byte line (64-byte pieces halve the copy rate).  Two waves per SIMD
-// are needed for the matrix pipe to issue at full rate.
-using W13Cfg = fast::Cfg<fast::kW13, 256, 256, 64, 2, 2, 4>;
-using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4>;
+// w13: 256 rows x (128 gate + 128 up) B-rows, BK 64, 8 waves of 128 x 64;
+// down: the same shape with 256 output columns.  BK 64 keeps every row copy
+// a full 128-byte line (64-byte pieces halve the copy rate).  Two waves per
+// SIMD are needed for the 16x16x32 MFMA to issue at full rate.  Two slots of
+// gathered rows and three of weights fill the 160 KB of LDS: the weight
+// copies (from HBM) are issued two k-tiles ahead, the row copies one.
+using W13Cfg = fast::Cfg<fast::kW13, 256, 256, 64, 2, 2, 4, 3>;
+using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4, 3>;
 
 
 inline unsigned grid_size(long long tiles) {

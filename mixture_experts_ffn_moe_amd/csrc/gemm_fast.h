@@ -73,6 +73,19 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t 
                :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
+// Workgroup barrier for the k loop.  __syncthreads() carries a memory fence
+// that waits for every outstanding global load, including the direct-to-LDS
+// copies still in flight for later k-tiles; this one waits only for the
+// wave's LDS reads (so the slot they read may be refilled) and the copies the
+// caller has already waited for.  The scheduling barriers keep the compiler
+// from moving work across it.
+__device__ __forceinline__ void kloop_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 struct Tile {
   int e, m0, seg_end, nt, valid;
 };
@@ -327,7 +340,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
           wait_vmcnt<(C::STAGES - 2) * C::NI>();
         else
           wait_vmcnt<0>();
-        __syncthreads();
+        kloop_barrier();
         if (kt + C::STAGES - 1 < KT) {
           issue_a(kt + C::STAGES - 1);
           issue_b(kt + C::STAGES - 1);
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
           wait_vmcnt<C::B_PER_WAVE>();  // B(kt+1) may stay in flight
         else
           wait_vmcnt<0>();
-        __syncthreads();
+        kloop_barrier();
         if (kt + 1 < KT) issue_a(kt + 1);
         if (kt + 2 < KT) issue_b(kt + 2);
       }

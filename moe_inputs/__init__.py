@@ -108,8 +108,8 @@ class LayerInputs:
     meta: dict = field(default_factory=dict)
 
 
-# The five layer calls of the workload (index order is fixed).
-CONFIGS = [
+# The five layers of the workload, by name.
+LAYERS = [
     LayerSpec("tiny_fp32", T=64, H=256, E=8, k=2, Im=128, micro=1, dtype=F32,
               x_seed=0, layer_seed=0, sigma_g=0.1,
               note="tiny fp32 correctness layer"),
@@ -128,13 +128,11 @@ CONFIGS = [
 ]
 
 
-def spec(i_or_name) -> LayerSpec:
-    if isinstance(i_or_name, int):
-        return CONFIGS[i_or_name]
-    for s in CONFIGS:
-        if s.name == i_or_name:
+def spec(name: str) -> LayerSpec:
+    for s in LAYERS:
+        if s.name == name:
             return s
-    raise KeyError(i_or_name)
+    raise KeyError(name)
 
 
 def zipf_bias(E: int, s: float, scale: float, seed: int) -> np.ndarray:
@@ -180,7 +178,7 @@ def micro_pack_expert(sp: LayerSpec, w13: np.ndarray, down: np.ndarray):
 
 
 def expert_pack(sp: LayerSpec, e: int):
-    """Return (w1[m] [2Im,H], w2[m] [H,Im]) for expert e in the config's dtype."""
+    """Return (w1[m] [2Im,H], w2[m] [H,Im]) for expert e in the layer's dtype."""
     w13, down = expert_weights_unsharded(sp, e)
     w1s, w2s = micro_pack_expert(sp, w13, down)
     return [_cast(sp, a) for a in w1s], [_cast(sp, a) for a in w2s]

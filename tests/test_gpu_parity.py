@@ -86,7 +86,7 @@ def check_routing(sp, inp, got, ref):
 # ------------------------------------------------------------------ small layers
 
 SMALL = [
-    dict(name="tiny_fp32", cfg=0),
+    dict(name="tiny_fp32", layer="tiny_fp32"),
     dict(name="bf16_one_tile", T=300, H=256, E=8, k=2, Im=128, micro=2, dtype=mi.BF16, seed=11),
     dict(name="bf16_ragged", T=1000, H=512, E=6, k=3, Im=256, micro=1, dtype=mi.BF16, seed=12),
     dict(name="bf16_skewed_empty", T=700, H=256, E=16, k=4, Im=128, micro=2, dtype=mi.BF16, seed=13,
@@ -108,8 +108,8 @@ SMALL = [
 def small_spec(c):
     c = dict(c)
     name = c.pop("name")
-    if "cfg" in c:
-        return mi.spec(c["cfg"])
+    if "layer" in c:
+        return mi.spec(c["layer"])
     zipf = c.pop("zipf", None)
     sp = mi.custom_spec(zipf=zipf, name=name, **c)
     return sp
@@ -161,7 +161,7 @@ def test_small_layer_stepwise_and_forward(m, case):
 
 
 def test_tiny_runs_are_bitwise_reproducible(m):
-    sp = mi.spec(0)
+    sp = mi.spec("tiny_fp32")
     inp = mi.make_layer(sp)
     d = device_inputs(inp)
     a = run_steps(m, sp, d)
@@ -213,14 +213,14 @@ def test_routing_ties_toward_lower_expert(m):
 _CACHE = {}
 
 
-def full_layer(i):
-    """Seeded inputs of config i; configs 1, 2 and 4 share one layer's
-    weights (2 and 4 hold them micro-major), generated once."""
-    if i in _CACHE:
-        return _CACHE[i]
-    sp = mi.spec(i)
-    if i in (2, 4) and 1 in _CACHE:
-        base = _CACHE[1]
+def full_layer(name):
+    """Seeded inputs of a full-size layer; the 2-micro and skewed layers hold
+    the 1-micro layer's weights micro-major (generated once)."""
+    if name in _CACHE:
+        return _CACHE[name]
+    sp = mi.spec(name)
+    if name in ("denoise_2micro", "skewed_cfg") and "denoise_1micro" in _CACHE:
+        base = _CACHE["denoise_1micro"]
         w1 = np.empty((2, sp.E, 2 * sp.Im, sp.H), np.uint16)
         w2 = np.empty((2, sp.E, sp.H, sp.Im), np.uint16)
         I, Im = 1536, 768
@@ -228,12 +228,12 @@ def full_layer(i):
             w1[mm, :, :Im] = base.w1[0, :, mm * Im:(mm + 1) * Im]
             w1[mm, :, Im:] = base.w1[0, :, I + mm * Im:I + (mm + 1) * Im]
             w2[mm] = base.w2[0, :, :, mm * Im:(mm + 1) * Im]
-        x = base.x if i == 2 else mi.make_x(sp)
+        x = base.x if name == "denoise_2micro" else mi.make_x(sp)
         wg, bias = mi.make_router(sp)
         inp = mi.LayerInputs(sp, x, wg, bias, w1, w2)
     else:
         inp = mi.make_layer(sp)
-    _CACHE[i] = inp
+    _CACHE[name] = inp
     return inp
 
 
@@ -243,11 +243,11 @@ def sample_tokens(T, n=16, seed=0):
     return sorted(s)
 
 
-@pytest.mark.parametrize("i", [1, 2, 3, 4])
-def test_full_size_forward(m, i):
-    sp = mi.spec(i)
-    say(f"[parity] full-size config {sp.name}: T={sp.T} E={sp.E} k={sp.k} Im={sp.Im} mu={sp.micro}")
-    inp = full_layer(i)
+@pytest.mark.parametrize("name", ["denoise_1micro", "denoise_2micro", "decode", "skewed_cfg"])
+def test_full_size_forward(m, name):
+    sp = mi.spec(name)
+    say(f"[parity] full-size layer {sp.name}: T={sp.T} E={sp.E} k={sp.k} Im={sp.Im} mu={sp.micro}")
+    inp = full_layer(name)
     ref = o.route(inp)
     d = device_inputs(inp)
     from mixture_experts_ffn_moe_amd import MoELayerBuffers
@@ -256,7 +256,7 @@ def test_full_size_forward(m, i):
     torch.cuda.synchronize()
     v = buf.views()
     check_routing(sp, inp, v, ref)
-    if i == 4:
+    if name == "skewed_cfg":
         counts = ref["counts"]
         assert (counts == 0).any()
         say(f"[parity] skewed loads: max {counts.max()} empty {(counts == 0).sum()}")
@@ -269,19 +269,19 @@ def test_full_size_forward(m, i):
     out2 = MoELayerBuffers(shape_of(sp)).forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
-    _CACHE[f"out{i}"] = to_host_f32(out)
+    _CACHE["out_" + name] = to_host_f32(out)
     del d, buf
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("i", [1, 4])
-def test_full_size_stepwise_permute_matches_forward(m, i):
+@pytest.mark.parametrize("name", ["denoise_1micro", "skewed_cfg"])
+def test_full_size_stepwise_permute_matches_forward(m, name):
     """moe_permute (every workgroup recounts all ids, several id tiles per
     wave at these sizes) against the one-call layer's permutation (built
     from the router's per-block counts): the same bits."""
-    sp = mi.spec(i)
+    sp = mi.spec(name)
     say(f"[parity] full-size step-wise permute {sp.name}: R={sp.T * sp.k}")
-    inp = full_layer(i)
+    inp = full_layer(name)
     d = device_inputs(inp)
     from mixture_experts_ffn_moe_amd import MoELayerBuffers
     buf = MoELayerBuffers(shape_of(sp))
@@ -302,9 +302,9 @@ def test_full_size_stepwise_permute_matches_forward(m, i):
 def test_two_micro_equals_one_micro_full_size(m):
     """The 2-micro layer (micro-major pack) must equal the expert-major layer
     within tolerance over every output element."""
-    if "out1" not in _CACHE or "out2" not in _CACHE:
-        pytest.skip("needs the full-size runs of configs 1 and 2 in this session")
-    assert_close(_CACHE["out2"], _CACHE["out1"], mi.BF16, "2-micro vs 1-micro")
+    if "out_denoise_1micro" not in _CACHE or "out_denoise_2micro" not in _CACHE:
+        pytest.skip("needs the full-size runs of the 1-micro and 2-micro layers in this session")
+    assert_close(_CACHE["out_denoise_2micro"], _CACHE["out_denoise_1micro"], mi.BF16, "2-micro vs 1-micro")
 
 
 def test_micro_views_sum_to_multi_micro(m):

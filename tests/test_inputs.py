@@ -32,7 +32,7 @@ def test_seeds_reproduce_and_differ():
 def test_two_micro_pack_is_relayout_of_expert_major():
     """The 2-micro layer holds exactly the 1-micro layer's weights, stored
     micro-major with the [gate_m0, up_m0] / [gate_m1, up_m1] order."""
-    s1, s2 = mi.spec(1), mi.spec(2)
+    s1, s2 = mi.spec("denoise_1micro"), mi.spec("denoise_2micro")
     for e in (0, 37):
         a1, b1 = mi.expert_pack(s1, e)
         a2, b2 = mi.expert_pack(s2, e)
@@ -44,20 +44,20 @@ def test_two_micro_pack_is_relayout_of_expert_major():
             assert np.array_equal(b2[m], down[:, m * Im:(m + 1) * Im])
 
 
-def test_config_table():
-    assert [s.name for s in mi.CONFIGS] == ["tiny_fp32", "denoise_1micro", "denoise_2micro",
+def test_layer_table():
+    assert [s.name for s in mi.LAYERS] == ["tiny_fp32", "denoise_1micro", "denoise_2micro",
                                            "decode", "skewed_cfg"]
-    s = mi.spec(1)
+    s = mi.spec("denoise_1micro")
     assert (s.T, s.H, s.E, s.k, s.I) == (4096, 4096, 64, 8, 1536)
-    assert mi.spec(2).I == 1536 and mi.spec(2).micro == 2
-    assert mi.spec(3).T == 8 and mi.spec(3).I == 768
-    assert mi.spec(4).T == 8192
+    assert mi.spec("denoise_2micro").I == 1536 and mi.spec("denoise_2micro").micro == 2
+    assert mi.spec("decode").T == 8 and mi.spec("decode").I == 768
+    assert mi.spec("skewed_cfg").T == 8192
 
 
-def test_skewed_config_leaves_experts_empty():
+def test_skewed_layer_leaves_experts_empty():
     """Route the skewed layer with the oracle: the bias must produce a heavy
     head and some empty experts."""
-    sp = mi.spec(4)
+    sp = mi.spec("skewed_cfg")
     x32 = o.widen(mi.make_x(sp), sp.dtype)
     wg, bias = mi.make_router(sp)
     ids = o.select_topk(o.router_logits(x32, wg, bias), sp.k)
@@ -68,7 +68,7 @@ def test_skewed_config_leaves_experts_empty():
 
 
 def test_near_uniform_denoise_routing():
-    sp = mi.spec(1)
+    sp = mi.spec("denoise_1micro")
     x32 = o.widen(mi.make_x(sp), sp.dtype)
     wg, bias = mi.make_router(sp)
     assert bias is None

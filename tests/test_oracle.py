@@ -271,8 +271,8 @@ def test_forward_matches_dense_bruteforce(cfg):
         assert (r["counts"] == 0).any(), "skewed bias should leave an expert empty"
 
 
-def test_tiny_config_matches_dense_bruteforce():
-    inp = mi.make_layer(0)
+def test_tiny_layer_matches_dense_bruteforce():
+    inp = mi.make_layer("tiny_fp32")
     r = o.forward(inp)
     w13s, downs = _unsharded(inp)
     ref = o.brute_dense(o.widen(inp.x, inp.spec.dtype), r["ids"], r["w"], w13s, downs)
