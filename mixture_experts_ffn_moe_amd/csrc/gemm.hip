@@ -132,10 +132,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 // w13: 256 rows x (128 gate + 128 up) B-rows, BK 64, 8 waves of 128 x 64;
 // down: the same shape with 256 output columns.  BK 64 keeps every row copy
 // a full 128-byte line (64-byte pieces halve the copy rate).  Two waves per
-// SIMD are needed for the 16x16x32 MFMA to issue at full rate.  Two slots of
-// gathered rows and three of weights fill the 160 KB of LDS: the weight
-// copies (from HBM) are issued two k-tiles ahead, the row copies one.
-using W13Cfg = fast::Cfg<fast::kW13, 256, 256, 64, 2, 2, 4, 3>;
+// SIMD are needed for the 16x16x32 MFMA to issue at full rate.  The down
+// GEMM keeps three weight slots (2 x 32 KB of h rows + 3 x 32 KB of weights
+// fill the 160 KB of LDS), so its weight copies run two k-tiles ahead; for
+// w13 the third slot measured no faster and raised its fabric reads by 16%
+// (the m-tiles that share a weight tile drift further apart).
+using W13Cfg = fast::Cfg<fast::kW13, 256, 256, 64, 2, 2, 4, 2>;
 using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4, 3>;
 
 
