@@ -16,10 +16,12 @@
 //      the ascending list of active experts.
 //   3. decode_w13: one workgroup per (active expert, 64 columns of the
 //      micro-major intermediate); each wave streams 16 gate and 16 up rows of
-//      w1 straight from memory into MFMA B fragments (M = the expert's rows,
-//      padded to 16) and applies SwiGLU; h is rounded to bf16.
+//      w1 in whole 128-byte lines, re-lays them through LDS into MFMA B
+//      fragments (M = the expert's rows, padded to 16) and applies SwiGLU; h
+//      is rounded to bf16.
 //   4. decode_down_finalize: one workgroup per 16 output columns; its eight
-//      waves split the active experts (enough loads in flight per CU), stream the matching w2 rows, and put
+//      waves split the active experts (enough loads in flight per CU), stream
+//      the matching w2 rows the same way, and put
 //      w[t, j] * y[route (t, j)] into a per-route LDS slot; the slots are then
 //      summed in ascending j (the finalize of section 6.1), so the down
 //      partials of every micro-shard and route are reduced once, without
@@ -218,10 +220,36 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
 }
 
 // ---------------------------------------------------------------------------
-// 3. gate|up + SwiGLU for one active expert and 64 intermediate columns.
-constexpr int kUnroll = 8;     // k-steps of 32 in flight per wave
-constexpr int kDownWaves = 8;  // waves of the down+finalize workgroup (they split the experts)
+// Weight streaming.  A wave reads 16 weight rows per 64-element k-step as two
+// loads of 8 rows x 128 bytes (eight lanes per row: every load covers whole
+// 128-byte lines, which HBM serves markedly faster than the 64-byte halves
+// the MFMA fragment layout would ask for), writes them to a per-wave LDS
+// buffer and reads them back in the 16x16x32 B-fragment layout (lane l: row
+// l % 16, 8 consecutive k of chunk l / 16).  Within a 128-byte row the 16-byte
+// chunks are XOR-swizzled by (row / 2) % 8, so the 16 lanes of one LDS phase
+// hit 16 bank groups on both sides.  The k order inside each MFMA is the one
+// the grouped GEMMs use, so h is the same bits on both paths.
+constexpr int kStep = 64;        // k per LDS round trip
+constexpr int kStepsW13 = 2;     // k-steps of 64 whose loads are in flight together (w13)
+constexpr int kStepsDown = 4;    // the same for the down projection
+constexpr int kDownWaves = 16;   // waves of the down+finalize workgroup (they split the experts)
 
+struct WaveRows {
+  // byte offsets of this lane in a 16-row x 128-byte block: its load slot and
+  // its fragment-read slot for the two 32-element halves of a k-step
+  uint32_t wr0, wr1, rd0, rd1;
+  __device__ __forceinline__ explicit WaveRows(int lane) {
+    const int r0 = lane >> 3, r1 = 8 + (lane >> 3), c = lane & 7;
+    wr0 = (uint32_t)(r0 * 128 + ((c ^ ((r0 >> 1) & 7)) * 16));
+    wr1 = (uint32_t)(r1 * 128 + ((c ^ ((r1 >> 1) & 7)) * 16));
+    const int fr = lane & 15, g = lane >> 4;
+    rd0 = (uint32_t)(fr * 128 + (((0 + g) ^ ((fr >> 1) & 7)) * 16));
+    rd1 = (uint32_t)(fr * 128 + (((4 + g) ^ ((fr >> 1) & 7)) * 16));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// 3. gate|up + SwiGLU for one active expert and 64 intermediate columns.
 __global__ __launch_bounds__(256) void decode_w13(const uint16_t* __restrict__ x,
                                                   const int32_t* __restrict__ perm,
                                                   const int32_t* __restrict__ offsets,
@@ -229,6 +257,7 @@ __global__ __launch_bounds__(256) void decode_w13(const uint16_t* __restrict__ x
                                                   const uint16_t* __restrict__ w1, int H, int E,
                                                   int k, int Im, int mu, int ncg,
                                                   uint16_t* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) char buf[4][2][2048];  // per wave: gate, up
   const int a = blockIdx.x / ncg, cg = blockIdx.x % ncg;
   if (a >= active[kMaxExperts]) return;
   const int e = active[a];
@@ -237,29 +266,48 @@ __global__ __launch_bounds__(256) void decode_w13(const uint16_t* __restrict__ x
   const int c0 = cg * 64 + wave * 16;      // column in [0, mu*Im)
   const int micro = c0 / Im, i0 = c0 - micro * Im;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
+  const WaveRows wr(lane);
+  char* gb = buf[wave][0];
+  char* ub = buf[wave][1];
 
   const bool row_ok = fr < n;
   const uint16_t* arow = x + (size_t)(perm[seg + min(fr, n - 1)] / k) * H + fk;
   const uint16_t* wbase = w1 + (size_t)(micro * E + e) * 2 * Im * H;
-  const uint16_t* grow = wbase + (size_t)(i0 + fr) * H + fk;
-  const uint16_t* urow = wbase + (size_t)(Im + i0 + fr) * H + fk;
+  // rows lane/8 and 8 + lane/8 of the gate and up blocks, chunk lane % 8
+  const uint16_t* g0 = wbase + (size_t)(i0 + (lane >> 3)) * H + (lane & 7) * 8;
+  const uint16_t* u0 = wbase + (size_t)(Im + i0 + (lane >> 3)) * H + (lane & 7) * 8;
+  const size_t r8 = (size_t)8 * H;
 
   f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < H; k0 += 32 * kUnroll) {
-    uint4 av[kUnroll], gv[kUnroll], uv[kUnroll];
+  for (int k0 = 0; k0 < H; k0 += kStep * kStepsW13) {
+    uint4 gv[kStepsW13][2], uv[kStepsW13][2], av[kStepsW13][2];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      gv[u] = *reinterpret_cast<const uint4*>(grow + k0 + 32 * u);
-      uv[u] = *reinterpret_cast<const uint4*>(urow + k0 + 32 * u);
-      av[u] = *reinterpret_cast<const uint4*>(arow + k0 + 32 * u);
+    for (int q = 0; q < kStepsW13; ++q) {
+      const int kk = k0 + kStep * q;
+      gv[q][0] = *reinterpret_cast<const uint4*>(g0 + kk);
+      gv[q][1] = *reinterpret_cast<const uint4*>(g0 + r8 + kk);
+      uv[q][0] = *reinterpret_cast<const uint4*>(u0 + kk);
+      uv[q][1] = *reinterpret_cast<const uint4*>(u0 + r8 + kk);
+      av[q][0] = *reinterpret_cast<const uint4*>(arow + kk);
+      av[q][1] = *reinterpret_cast<const uint4*>(arow + kk + 32);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint4 aa = av[u];
-      if (!row_ok) aa = make_uint4(0, 0, 0, 0);
-      const bf16x8 A = __builtin_bit_cast(bf16x8, aa);
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, gv[u]), accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, uv[u]), accu, 0, 0, 0);
+    for (int q = 0; q < kStepsW13; ++q) {
+      *reinterpret_cast<uint4*>(gb + wr.wr0) = gv[q][0];
+      *reinterpret_cast<uint4*>(gb + wr.wr1) = gv[q][1];
+      *reinterpret_cast<uint4*>(ub + wr.wr0) = uv[q][0];
+      *reinterpret_cast<uint4*>(ub + wr.wr1) = uv[q][1];
+      const uint4 gf0 = *reinterpret_cast<const uint4*>(gb + wr.rd0);
+      const uint4 gf1 = *reinterpret_cast<const uint4*>(gb + wr.rd1);
+      const uint4 uf0 = *reinterpret_cast<const uint4*>(ub + wr.rd0);
+      const uint4 uf1 = *reinterpret_cast<const uint4*>(ub + wr.rd1);
+      uint4 a0 = av[q][0], a1 = av[q][1];
+      if (!row_ok) a0 = a1 = make_uint4(0, 0, 0, 0);
+      const bf16x8 A0 = __builtin_bit_cast(bf16x8, a0), A1 = __builtin_bit_cast(bf16x8, a1);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, gf0), accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, uf0), accu, 0, 0, 0);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, gf1), accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, uf1), accu, 0, 0, 0);
     }
   }
   // D layout: register r holds row 4*(lane/16) + r, column lane%16
@@ -280,34 +328,48 @@ __global__ __launch_bounds__(kDownWaves * 64) void decode_down_finalize(
     const float* __restrict__ topw, const uint16_t* __restrict__ w2, int T, int H, int E, int k,
     int Im, int mu, uint16_t* __restrict__ out) {
   __shared__ float slot[kDecT * kMaxK][16];
+  __shared__ __attribute__((aligned(16))) char buf[kDownWaves][2048];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const int n_act = active[kMaxExperts];
   const int K = mu * Im;
+  const WaveRows wr(lane);
+  char* wb = buf[wave];
+  const size_t r8 = (size_t)8 * Im;
 
   for (int a = wave; a < n_act; a += kDownWaves) {
     const int e = active[a];
     const int seg = offsets[e], n = offsets[e + 1] - seg;
     const bool row_ok = fr < n;
     const uint16_t* arow = h + (size_t)(seg + min(fr, n - 1)) * K + fk;
-    const uint16_t* brow = w2 + ((size_t)e * H + n0 + fr) * Im + fk;
+    // rows n0 + lane/8 and n0 + 8 + lane/8 of w2[.][e], chunk lane % 8
+    const uint16_t* b0 = w2 + ((size_t)e * H + n0 + (lane >> 3)) * Im + (lane & 7) * 8;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += 32 * kUnroll) {
-      uint4 av[kUnroll], bv[kUnroll];
+    for (int k0 = 0; k0 < K; k0 += kStep * kStepsDown) {
+      uint4 bv[kStepsDown][2], av[kStepsDown][2];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int kg = k0 + 32 * u;
+      for (int q = 0; q < kStepsDown; ++q) {
+        const int kg = k0 + kStep * q;  // a 64-step never crosses a micro boundary (Im % 256 == 0)
         const int mm = kg / Im;
-        bv[u] = *reinterpret_cast<const uint4*>(brow + (size_t)mm * E * H * Im + (kg - mm * Im));
-        av[u] = *reinterpret_cast<const uint4*>(arow + kg);
+        const uint16_t* bp = b0 + (size_t)mm * E * H * Im + (kg - mm * Im);
+        bv[q][0] = *reinterpret_cast<const uint4*>(bp);
+        bv[q][1] = *reinterpret_cast<const uint4*>(bp + r8);
+        av[q][0] = *reinterpret_cast<const uint4*>(arow + kg);
+        av[q][1] = *reinterpret_cast<const uint4*>(arow + kg + 32);
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        uint4 aa = av[u];
-        if (!row_ok) aa = make_uint4(0, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
-                                                      __builtin_bit_cast(bf16x8, bv[u]), acc, 0, 0, 0);
+      for (int q = 0; q < kStepsDown; ++q) {
+        *reinterpret_cast<uint4*>(wb + wr.wr0) = bv[q][0];
+        *reinterpret_cast<uint4*>(wb + wr.wr1) = bv[q][1];
+        const uint4 f0 = *reinterpret_cast<const uint4*>(wb + wr.rd0);
+        const uint4 f1 = *reinterpret_cast<const uint4*>(wb + wr.rd1);
+        uint4 a0 = av[q][0], a1 = av[q][1];
+        if (!row_ok) a0 = a1 = make_uint4(0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                      __builtin_bit_cast(bf16x8, f0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                      __builtin_bit_cast(bf16x8, f1), acc, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -337,8 +399,8 @@ size_t decode_scratch_bytes() {
 
 bool decode_supported(const Shape& s) {
   return s.bf16 && s.T >= 1 && s.T <= kDecT && s.k <= kMaxK && (s.H % (kSplit * 128)) == 0 &&
-         (s.Im % 64) == 0 && (s.mu * s.Im) % 64 == 0 && (s.H % (32 * kUnroll)) == 0 &&
-         (s.Im % (32 * kUnroll)) == 0 && (s.H % 16) == 0;
+         (s.Im % 64) == 0 && (s.mu * s.Im) % 64 == 0 && (s.H % (kStep * kStepsW13)) == 0 &&
+         (s.Im % (kStep * kStepsDown)) == 0 && (s.H % 16) == 0;
 }
 
 hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const float* bias,
