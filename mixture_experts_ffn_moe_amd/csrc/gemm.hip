@@ -128,16 +128,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
   }
 }
 
-// bf16 tile configurations (measured on MI355X for the denoise layer):
-// w13: 256 rows x (128 gate + 128 up) B-rows, BK 64, 8 waves of 128 x 64;
-// down: the same shape with 256 output columns.  BK 64 keeps every row copy
-// a full 128-byte line (64-byte pieces halve the copy rate).  Two waves per
-// SIMD are needed for the 16x16x32 MFMA to issue at full rate.  The down
-// GEMM keeps three weight slots (2 x 32 KB of h rows + 3 x 32 KB of weights
-// fill the 160 KB of LDS), so its weight copies run two k-tiles ahead; for
-// w13 the third slot measured no faster and raised its fabric reads by 16%
-// (the m-tiles that share a weight tile drift further apart).
-using W13Cfg = fast::Cfg<fast::kW13, 256, 256, 64, 2, 2, 4, 2>;
+// bf16 tile configurations (measured on MI355X for the denoise layer, the
+// variants interleaved in one process on random data):
+// w13: 320 rows x (128 gate + 128 up) B-rows, BK 64, 8 waves of 160 x 64;
+// down: 256 rows x 256 output columns, 8 waves of 128 x 64.  BK 64 keeps
+// every row copy a full 128-byte line (64-byte pieces halve the copy rate).
+// Two waves per SIMD are needed for the 16x16x32 MFMA to issue at full rate.
+//  * 320-row tiles cover an expert of up to 640 routes in two m-tiles (256-row
+//    tiles need three once an expert passes 512, and each extra m-tile streams
+//    the expert's weight tile again): 2.3% faster for w13 at the near-uniform
+//    loads of the denoise layer.  For down the 256-row tile with a third weight
+//    slot is as fast (LDS: 2 x 32 KB of h rows + 3 x 32 KB of weights).
+//  * w13 keeps two weight slots: the third measured no faster and raised its
+//    fabric reads by 16% (the m-tiles that share a weight tile drift apart).
+using W13Cfg = fast::Cfg<fast::kW13, 320, 256, 64, 2, 2, 4, 2>;
 using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4, 3>;
 
 

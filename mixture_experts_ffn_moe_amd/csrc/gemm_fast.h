@@ -30,7 +30,9 @@ struct Cfg {
   // ring slots of the B (weight) tiles; A keeps STAGES.  SB = STAGES + 1 gives
   // the HBM-streamed weights one more k-tile of lead than the gathered rows.
   static constexpr int SB = SB_;
-  static_assert(SB == STAGES || (STAGES == 2 && SB == 3), "ring depths");
+  // two row slots: the waits in the k loop count only weight copies as
+  // possibly in flight, which the skipped row copies of short tiles rely on
+  static_assert(STAGES == 2 && (SB == 2 || SB == 3), "ring depths");
   static constexpr int WM = WM_, WN = WN_;
   static constexpr int NW = WM * WN;
   static constexpr int NTHR = NW * 64;
@@ -257,12 +259,18 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
   const uint32_t ldsA = (uint32_t)(uintptr_t)smem;
   const uint32_t ldsB = ldsA + (uint32_t)(C::STAGES * A_SLOT) * 2u;
 
+  // Row groups past the tile's rows (rounded up to the 16-row MFMA
+  // fragments) are never read: their copies are skipped.  The waits below
+  // only ever leave weight copies in flight, so they hold with any number of
+  // row copies.
+  const int a_rows = PART ? __builtin_amdgcn_readfirstlane(min(C::BM, (ti.seg_end - ti.m0 + 15) & ~15)) : C::BM;
   auto issue_a = [&](int kt) {
     const uint32_t sb = ldsA + (uint32_t)((kt % C::STAGES) * A_SLOT) * 2u;
     const uint16_t* abase = A + kt * C::BK;
 #pragma unroll
     for (int i = 0; i < C::A_PER_WAVE; ++i)
-      dma16(sb + (uint32_t)((wave + C::NW * i) * C::RPI * C::BK) * 2u, abase, a_off[i]);
+      if ((wave + C::NW * i) * C::RPI < a_rows)
+        dma16(sb + (uint32_t)((wave + C::NW * i) * C::RPI * C::BK) * 2u, abase, a_off[i]);
   };
   auto issue_b = [&](int kt) {
     const int kg = kt * C::BK;
