@@ -159,6 +159,40 @@ def time_forward(moe, torch, d, steps, warmup):
     return ev_ms, wall_ms, buf
 
 
+def time_two_dispatch(moe, torch, d, steps, warmup, ms_multi):
+    """Ablation of the multi-micro layer: each micro view of the micro-major
+    pack run as its own one-micro layer call (routing, permutation, both
+    GEMMs and finalize per micro), the two bf16 partial outputs added in fp32
+    and rounded once (torch adds them: the ablation arm's own reduction,
+    outside the layer), against the one multi-micro call that shares routing,
+    permutation and finalize.  Both arms consume the same resident weights."""
+    sp = d["sp"]
+    vshape = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, 1, sp.dtype)
+    b0, b1 = moe.MoELayerBuffers(vshape), moe.MoELayerBuffers(vshape)
+    views = [(d["w1"][m], d["w2"][m]) for m in range(sp.micro)]
+    assert sp.micro == 2 and all(w.is_contiguous() for pair in views for w in pair)
+    out = torch.empty(sp.T, sp.H, dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        o0 = b0.forward(d["x"], d["wg"], d["bias"], *views[0])
+        o1 = b1.forward(d["x"], d["wg"], d["bias"], *views[1])
+        out.copy_(o0.float() + o1.float())
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_two_dispatch": round(ms, 4), "ms_multi_micro": round(ms_multi, 4),
+            "saving_ms": round(ms - ms_multi, 4), "saving_frac": round((ms - ms_multi) / ms, 4),
+            "note": "two one-micro calls on the micro views + fp32 add of the partials vs one 2-micro call"}
+
+
 def time_kernels(moe, torch, d, steps, warmup):
     """Per-kernel average durations (ms): the same five kernels through the
     step-wise entry points, each bracketed by HIP events on the launch
@@ -303,6 +337,15 @@ def main(argv=None):
         print(json.dumps({"decode": dec}), flush=True)
         return 0
 
+    decode = None
+    if not args.no_extra:
+        # AR decode first, before the denoise layers' multi-GB buffers are
+        # allocated and freed (resident weights in a server are allocated once)
+        decode = time_decode(moe, torch, max(args.steps, 50), args.warmup)
+        log(f"decode {decode['ms'] * 1e3:.1f} us, {decode['GB_per_s']:.0f} GB/s, "
+            f"{decode['active_experts']} active experts")
+        torch.cuda.empty_cache()
+
     sp = mi.spec("denoise_1micro")
     log(f"generating {sp.name}")
     base = mi.make_layer(sp)
@@ -360,6 +403,10 @@ def main(argv=None):
                                    "tokens_per_s": round(sp2.T / (ms2 * 1e-3), 1)}
         log(f"2-micro {ms2:.4f} ms")
         del b2
+        # two-dispatch arm: the same 2-micro pack as two one-micro layer calls on
+        # its micro views, partial outputs added
+        extra["two_dispatch_ablation"] = time_two_dispatch(moe, torch, d2, args.steps, args.warmup, ms2)
+        log(f"two-dispatch {extra['two_dispatch_ablation']['ms_two_dispatch']:.4f} ms")
         # skewed CFG batch (same 2-micro weights, T=8192, Zipf bias)
         sp4 = mi.spec("skewed_cfg")
         wg4, bias4 = mi.make_router(sp4)
@@ -374,10 +421,7 @@ def main(argv=None):
         log(f"skewed {ms4:.4f} ms")
         del d2, d4, b4buf
         torch.cuda.empty_cache()
-        # AR decode
-        extra["decode"] = time_decode(moe, torch, max(args.steps, 50), args.warmup)
-        log(f"decode {extra['decode']['ms'] * 1e3:.1f} us, {extra['decode']['GB_per_s']:.0f} GB/s, "
-            f"{extra['decode']['active_experts']} active experts")
+        extra["decode"] = decode
         res["other_layers"] = extra
 
     if not args.no_cpu:
