@@ -93,6 +93,29 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _layer_dtype(shape) -> torch.dtype:
+    return torch.bfloat16 if shape.dtype == MOE_BF16 else torch.float32
+
+
+def _arg(name: str, t, dtype: torch.dtype, numel: int, nullable: bool = False):
+    """Check one tensor argument against the element type and element count
+    the C entry point will read or write through its raw pointer (the library
+    cannot check sizes itself), then return the pointer."""
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name}: a tensor is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel} for this shape")
+    return _ptr(t)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -115,34 +138,69 @@ def moe_get_workspace_layout(shape: MoeShape) -> dict:
 
 
 def moe_route(shape, x, wg, bias, logits, topk_ids, topk_w, stream=None):
-    _check(lib.moe_route(ctypes.byref(shape), _ptr(x), _ptr(wg), _ptr(bias), _ptr(logits),
-                         _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "moe_route")
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    dt = _layer_dtype(shape)
+    _check(lib.moe_route(ctypes.byref(shape), _arg("x", x, dt, T * H), _arg("wg", wg, torch.float32, E * H),
+                         _arg("gate_bias", bias, torch.float32, E, nullable=True),
+                         _arg("logits", logits, torch.float32, T * E),
+                         _arg("topk_ids", topk_ids, torch.int32, T * k),
+                         _arg("topk_w", topk_w, torch.float32, T * k), _stream(stream)), "moe_route")
 
 
 def moe_permute(shape, topk_ids, counts, offsets, perm, inv, x=None, permuted_x=None, stream=None):
-    _check(lib.moe_permute(ctypes.byref(shape), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
-                           _ptr(perm), _ptr(inv), _ptr(x), _ptr(permuted_x), _stream(stream)),
+    T, H, E, k = shape.T, shape.H, shape.E, shape.k
+    R = T * k
+    dt = _layer_dtype(shape)
+    _check(lib.moe_permute(ctypes.byref(shape), _arg("topk_ids", topk_ids, torch.int32, R),
+                           _arg("counts", counts, torch.int32, E), _arg("offsets", offsets, torch.int32, E + 1),
+                           _arg("perm", perm, torch.int32, R), _arg("inv", inv, torch.int32, R),
+                           _arg("x", x, dt, T * H, nullable=True),
+                           _arg("permuted_x", permuted_x, dt, R * H, nullable=True), _stream(stream)),
            "moe_permute")
 
 
 def moe_grouped_gemm_w13_swiglu(shape, x, perm, offsets, w1, h, stream=None):
-    _check(lib.moe_grouped_gemm_w13_swiglu(ctypes.byref(shape), _ptr(x), _ptr(perm), _ptr(offsets),
-                                           _ptr(w1), _ptr(h), _stream(stream)),
+    T, H, E, k, Im, mu = shape.T, shape.H, shape.E, shape.k, shape.Im, shape.micro_count
+    R = T * k
+    dt = _layer_dtype(shape)
+    _check(lib.moe_grouped_gemm_w13_swiglu(ctypes.byref(shape), _arg("x", x, dt, T * H),
+                                           _arg("perm", perm, torch.int32, R),
+                                           _arg("offsets", offsets, torch.int32, E + 1),
+                                           _arg("w1", w1, dt, mu * E * 2 * Im * H),
+                                           _arg("h", h, dt, R * mu * Im), _stream(stream)),
            "moe_grouped_gemm_w13_swiglu")
 
 
 def moe_grouped_gemm_down(shape, h, offsets, w2, y, stream=None):
-    _check(lib.moe_grouped_gemm_down(ctypes.byref(shape), _ptr(h), _ptr(offsets), _ptr(w2), _ptr(y),
+    T, H, E, k, Im, mu = shape.T, shape.H, shape.E, shape.k, shape.Im, shape.micro_count
+    R = T * k
+    dt = _layer_dtype(shape)
+    _check(lib.moe_grouped_gemm_down(ctypes.byref(shape), _arg("h", h, dt, R * mu * Im),
+                                     _arg("offsets", offsets, torch.int32, E + 1),
+                                     _arg("w2", w2, dt, mu * E * H * Im), _arg("y", y, dt, R * H),
                                      _stream(stream)), "moe_grouped_gemm_down")
 
 
 def moe_finalize(shape, y, inv, topk_w, out, stream=None):
-    _check(lib.moe_finalize(ctypes.byref(shape), _ptr(y), _ptr(inv), _ptr(topk_w), _ptr(out),
+    T, H, k = shape.T, shape.H, shape.k
+    R = T * k
+    dt = _layer_dtype(shape)
+    _check(lib.moe_finalize(ctypes.byref(shape), _arg("y", y, dt, R * H), _arg("inv", inv, torch.int32, R),
+                            _arg("topk_w", topk_w, torch.float32, R), _arg("out", out, dt, T * H),
                             _stream(stream)), "moe_finalize")
 
 
 def moe_forward(shape, x, wg, bias, w1, w2, out, workspace, stream=None):
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.moe_forward(ctypes.byref(shape), _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w2),
-                           _ptr(out), _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream)),
+    T, H, E, Im, mu = shape.T, shape.H, shape.E, shape.Im, shape.micro_count
+    dt = _layer_dtype(shape)
+    if workspace is None:
+        raise ValueError("workspace: a tensor is required")
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.moe_forward(ctypes.byref(shape), _arg("x", x, dt, T * H), _arg("wg", wg, torch.float32, E * H),
+                           _arg("gate_bias", bias, torch.float32, E, nullable=True),
+                           _arg("w1", w1, dt, mu * E * 2 * Im * H), _arg("w2", w2, dt, mu * E * H * Im),
+                           _arg("out", out, dt, T * H), _ptr(workspace), ctypes.c_size_t(nbytes),
+                           _stream(stream)),
            "moe_forward")

@@ -11,7 +11,8 @@
 //     row, so the 16 rows read by one MFMA fragment load hit 16 distinct
 //     16-byte bank groups.
 //   * WM x WN waves, each owning a (BM/WM) x (BN/WN) block of 16x16 MFMA
-//     tiles (v_mfma_f32_16x16x32_bf16), accumulators in AGPRs.
+//     tiles (v_mfma_f32_16x16x32_bf16); two waves per SIMD, so a wave's
+//     accumulators and fragments share 256 registers.
 #pragma once
 
 #include "moe_common.h"

@@ -125,3 +125,27 @@ def test_binding_raises_on_error(m):
     with pytest.raises(m.MoeError) as ei:
         m._lib._check(m._lib.lib.moe_route(ctypes.byref(s), None, None, None, None, None, None, None), "moe_route")
     assert ei.value.code == m.MOE_ERR_UNSUPPORTED
+
+
+def test_binding_checks_tensors_before_the_call(m):
+    """The C entry points take raw pointers and cannot check sizes, so the
+    binding checks each tensor's device, dtype and element count against the
+    shape before calling (a wrong-size tensor would otherwise be written out
+    of bounds on the GPU)."""
+    torch = pytest.importorskip("torch")
+    s = m.make_shape(4, 256, 8, 2, 128, 1, "bf16")
+    f = m._lib._arg
+    assert f("bias", None, torch.float32, 8, nullable=True) is None
+    with pytest.raises(ValueError, match="required"):
+        f("x", None, torch.bfloat16, 4 * 256)
+    with pytest.raises(TypeError):
+        f("x", [0.0] * 1024, torch.bfloat16, 4 * 256)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        f("x", torch.zeros(4, 256, dtype=torch.bfloat16), torch.bfloat16, 4 * 256)
+    # every wrapper checks before it calls the library: host tensors are refused
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    wg = torch.zeros(8, 256)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        m.moe_route(s, x, wg, None, torch.zeros(4, 8), torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
+    with pytest.raises(ValueError, match="workspace"):
+        m.moe_forward(s, x, wg, None, x, x, x, None)
