@@ -49,15 +49,17 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 }
 
 // Logit tile of kTokTile tokens x 64 experts on the fp64 matrix pipe
-// (v_mfma_f64_16x16x4_f64, exact products, fp64 sums).  Eight waves, two per
-// SIMD (a single wave cannot keep the matrix pipe busy): wave w covers the
-// hidden quarter hw = w%4, [hw*H/4, (hw+1)*H/4), for the 16-expert tiles
-// q = 2*(w/4) and 2*(w/4)+1; lane (t = lane%16, g = lane/16) holds
-// x[t][h0 + 8g + m] and wg[16q + t][h0 + 8g + m] as the m-th MFMA's A and B
-// elements, so the 8 MFMAs of a 32-wide chunk sum every h of the chunk
-// exactly once.  The four quarter partials are added in a fixed order, so the
-// logits are reproducible run to run.
-constexpr int kRouteWaves = 8;
+// (v_mfma_f64_16x16x4_f64, exact products, fp64 sums).  Sixteen waves, four
+// per SIMD (one wave alone cannot keep the matrix pipe busy, and four hide the
+// activation loads from HBM better than two): wave w covers the hidden eighth
+// hw = w % 8, [hw*H/8, (hw+1)*H/8), for the 16-expert tiles q = 2*(w/8) and
+// 2*(w/8)+1; lane (t = lane%16, g = lane/16) holds x[t][h0 + 8g + m] and
+// wg[16q + t][h0 + 8g + m] as the m-th MFMA's A and B elements, so the 8
+// MFMAs of a 32-wide chunk sum every h of the chunk exactly once.  The eight
+// partials are added in a fixed order, so the logits are reproducible run to
+// run.
+constexpr int kRouteWaves = 16;
+constexpr int kHParts = kRouteWaves / 2;  // hidden parts (each wave: one part, one expert half)
 
 template <typename XT>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __restrict__ x,
@@ -67,16 +69,16 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ topw,
                                                     int32_t* __restrict__ hist) {
-  __shared__ double part[4][kTokTile][kMaxExperts + 1];
+  __shared__ double part[kHParts][kTokTile][kMaxExperts + 1];
   __shared__ float lg[kTokTile][kMaxExperts];
   __shared__ int hcnt[kMaxExperts];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int hw = wave & 3, eh = wave >> 2;  // hidden quarter, expert half
+  const int hw = wave % kHParts, eh = wave / kHParts;  // hidden part, expert half
   const int t0 = blockIdx.x * kTokTile;
   const int tl = lane & 15, g = lane >> 4;
-  const int hq = H / 4;
+  const int hq = H / kHParts;
   const int hb = hw * hq;
 
   if (tid < kMaxExperts) hcnt[tid] = 0;  // ordered before its use by the barriers below
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
   for (int q = 0; q < 2; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // chunk loads are double-buffered: chunk c+32 is in flight while the
-  // 16 MFMAs of chunk c run (hq is a multiple of 64)
+  // 16 MFMAs of chunk c run (hq = H / kHParts is a multiple of 32)
   float xv[2][8], wv[2][2][8];
   auto load_chunk = [&](int c, int b) {
     load8(xrow + c, xv[b]);
@@ -115,7 +117,8 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
   // the scheduling barriers keep each prefetch ahead of the MFMAs it is
   // meant to overlap (left alone, the compiler sinks the loads to their use)
   load_chunk(0, 0);
-  for (int c = 0; c < hq; c += 64) {
+  int c = 0;
+  for (; c + 64 <= hq; c += 64) {
     load_chunk(c + 32, 1);
     __builtin_amdgcn_sched_barrier(0);
     mma_chunk(0);
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
     mma_chunk(1);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (c < hq) mma_chunk(0);  // trailing chunk (hq % 64 == 32), loaded above
   // fp64 16x16 D layout: register r of lane holds row (lane/16) + 4r (token),
   // column lane%16 (expert)
 #pragma unroll
@@ -137,7 +141,9 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
   for (int i = 0; i < kTokTile * kMaxExperts / (kRouteWaves * 64); ++i) {
     const int idx = tid + kRouteWaves * 64 * i;
     const int r = idx >> 6, e = idx & 63;
-    const double s = ((part[0][r][e] + part[1][r][e]) + part[2][r][e]) + part[3][r][e];
+    double s = part[0][r][e];
+#pragma unroll
+    for (int p = 1; p < kHParts; ++p) s += part[p][r][e];
     const double b = (bias != nullptr && e < E) ? (double)bias[e] : 0.0;
     const float L = (float)(s + b);
     lg[r][e] = L;
