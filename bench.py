@@ -159,6 +159,37 @@ def time_forward(moe, torch, d, steps, warmup):
     return ev_ms, wall_ms, buf
 
 
+def measure_peaks(moe, torch):
+    """The device's sustained bf16 matrix rate and HBM read rate, measured in
+    this run with the library's probes (moe_probe.h): the vendor peaks assume
+    the maximum engine clock, which sustained matrix work does not hold."""
+    sink_f = torch.zeros(1, dtype=torch.float32, device="cuda")
+    sink_i = torch.zeros(1, dtype=torch.int32, device="cuda")
+    iters = 60000
+    moe.moe_probe_mfma_bf16(iters, sink_f)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = sum(moe.moe_probe_mfma_bf16(iters, sink_f) for _ in range(3))
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    buf = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB, 8x the infinity cache
+    moe.moe_probe_read(buf, sink_i)
+    torch.cuda.synchronize()
+    e0.record()
+    nbytes = sum(moe.moe_probe_read(buf, sink_i) for _ in range(5))
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return {"bf16_mfma_tflops": round(tflops, 1), "hbm_read_GB_per_s": round(gbs, 1),
+            "bf16_frac_of_vendor": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "hbm_frac_of_vendor": round(gbs / PEAK_HBM_GBS, 4),
+            "method": "moe_probe_mfma_bf16 (32x32x16 MFMA loop, pseudo-random operands, 3 launches) and "
+                      "moe_probe_read (16-byte loads over 2 GiB, 5 launches), timed with HIP events"}
+
+
 def time_two_dispatch(moe, torch, d, steps, warmup, ms_multi):
     """Ablation of the multi-micro layer: each micro view of the micro-major
     pack run as its own one-micro layer call (routing, permutation, both
@@ -423,6 +454,14 @@ def main(argv=None):
         torch.cuda.empty_cache()
         extra["decode"] = decode
         res["other_layers"] = extra
+
+    peaks = measure_peaks(moe, torch)
+    res["measured_peaks"] = peaks
+    res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / peaks["bf16_mfma_tflops"], 4)
+    if "decode" in res.get("other_layers", {}):
+        dec = res["other_layers"]["decode"]
+        dec["frac_of_measured_read_peak"] = round(dec["GB_per_s"] / peaks["hbm_read_GB_per_s"], 4)
+    log(f"measured peaks: {peaks['bf16_mfma_tflops']} TFLOP/s bf16, {peaks['hbm_read_GB_per_s']} GB/s read")
 
     if not args.no_cpu:
         log(f"CPU oracle on {args.cpu_tokens} tokens")

@@ -11,6 +11,6 @@ from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE, MOE_F32, MOE_OK, MoeError, MoeShape, make_shape, moe_finalize,
     moe_forward, moe_get_workspace_layout, moe_grouped_gemm_down, moe_grouped_gemm_w13_swiglu,
-    moe_permute, moe_route, moe_workspace_size, status_string,
+    moe_permute, moe_probe_mfma_bf16, moe_probe_read, moe_route, moe_workspace_size, status_string,
 )
 from .layer import MoELayerBuffers, workspace_views  # noqa: F401

@@ -24,6 +24,8 @@ EXPORTED = (
     "moe_status_string", "moe_workspace_size", "moe_get_workspace_layout", "moe_route",
     "moe_permute", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_down", "moe_finalize",
     "moe_forward",
+    # measurement probes (moe_probe.h)
+    "moe_probe_mfma_bf16", "moe_probe_mfma_flops", "moe_probe_read",
 )
 
 
@@ -70,6 +72,12 @@ def _load():
     lib.moe_finalize.restype = i32
     lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_forward.restype = i32
+    lib.moe_probe_mfma_bf16.argtypes = [i32, P, P]
+    lib.moe_probe_mfma_bf16.restype = i32
+    lib.moe_probe_mfma_flops.argtypes = [i32]
+    lib.moe_probe_mfma_flops.restype = ctypes.c_double
+    lib.moe_probe_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.moe_probe_read.restype = i32
     return lib
 
 
@@ -204,3 +212,20 @@ def moe_forward(shape, x, wg, bias, w1, w2, out, workspace, stream=None):
                            _arg("out", out, dt, T * H), _ptr(workspace), ctypes.c_size_t(nbytes),
                            _stream(stream)),
            "moe_forward")
+
+
+def moe_probe_mfma_bf16(iterations: int, sink, stream=None) -> float:
+    """Enqueue the bf16 matrix-rate probe; returns the FLOPs it performs."""
+    _check(lib.moe_probe_mfma_bf16(int(iterations), _arg("sink", sink, torch.float32, 1), _stream(stream)),
+           "moe_probe_mfma_bf16")
+    return float(lib.moe_probe_mfma_flops(int(iterations)))
+
+
+def moe_probe_read(buf, sink, stream=None) -> int:
+    """Enqueue the streaming-read probe over all of `buf`; returns its bytes."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda":
+        raise ValueError("buf: must be a GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.moe_probe_read(_ptr(buf), ctypes.c_size_t(nbytes), _arg("sink", sink, torch.int32, 1),
+                              _stream(stream)), "moe_probe_read")
+    return nbytes

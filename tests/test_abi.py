@@ -10,7 +10,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -20,9 +21,11 @@ def m():
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -38,6 +41,18 @@ def test_library_exports_every_declared_symbol(m):
     for n in declared_functions():
         assert hasattr(lib, n), n
     assert set(declared_functions()) == set(m.EXPORTED)
+
+
+def test_probe_validation(m):
+    lib = m._lib.lib
+    P = ctypes.c_void_p(4096)
+    assert lib.moe_probe_mfma_bf16(0, P, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_probe_mfma_bf16(10, P, None) == m.MOE_ERR_INVALID_ARG  # not a multiple of 4
+    assert lib.moe_probe_mfma_bf16(12, None, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_probe_read(P, 0, P, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_probe_read(ctypes.c_void_p(4096 + 4), 1024, P, None) == m.MOE_ERR_UNSUPPORTED
+    assert lib.moe_probe_read(P, 1000, P, None) == m.MOE_ERR_UNSUPPORTED
+    assert lib.moe_probe_mfma_flops(3) == 256 * 8 * 8 * 32768 * 3
 
 
 def test_status_strings(m):
