@@ -32,7 +32,8 @@
  * MOE_F32); router weights, bias, logits and routing weights are always fp32.
  *
  * Envelope (MOE_ERR_UNSUPPORTED outside it): 1 <= E <= 64, H % 256 == 0,
- * Im % 128 == 0, R < 2^31, every size in elements < 2^31.
+ * Im % 128 == 0, R < 2^31, every size in elements < 2^31, one expert's w1
+ * block (2*Im*H elements of 2 bytes) < 4 GiB.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

@@ -31,8 +31,11 @@ moe_status check_shape(const moe_shape* sh, Shape* out) {
   const long long R = (long long)s.T * s.k;
   const long long I = (long long)s.micro_count * s.Im;
   const long long lim = (1ll << 31) - 1;
+  // the GEMMs address one expert's weight block (w1: 2*Im x H, w2: H x Im)
+  // with 32-bit byte offsets
+  const long long expert_w1_bytes = 4ll * s.Im * s.H;
   if (R > lim || I > lim || R * s.H > lim || R * I > lim || (long long)s.T * s.H > lim ||
-      (long long)s.micro_count * s.E * 2 * s.Im * s.H > lim * 8)
+      (long long)s.micro_count * s.E * 2 * s.Im * s.H > lim * 8 || expert_w1_bytes > 0xffffffffll)
     return MOE_ERR_UNSUPPORTED;
   if (out) {
     out->T = s.T; out->H = s.H; out->E = s.E; out->k = s.k; out->Im = s.Im;

@@ -126,6 +126,15 @@ def test_pointer_and_workspace_validation(m):
     assert lib.moe_permute(ctypes.byref(s), P, P, P, P, P, P, None, None) == m.MOE_ERR_INVALID_ARG
 
 
+def test_expert_block_over_4gib_is_unsupported(m):
+    # 4 * Im * H bytes = 4 * 32768 * 32768 = 2^32: one expert's w1 block does
+    # not fit the GEMMs' 32-bit offsets
+    s = m.make_shape(1, 32768, 1, 1, 32768, 1, "bf16")
+    assert m._lib.lib.moe_workspace_size(ctypes.byref(s)) == 0
+    s2 = m.make_shape(1, 32768, 1, 1, 16384, 1, "bf16")
+    assert m._lib.lib.moe_workspace_size(ctypes.byref(s2)) > 0
+
+
 def test_zero_tokens_is_a_no_op(m):
     lib = m._lib.lib
     s = m.make_shape(0, 256, 8, 2, 128, 1, "bf16")
