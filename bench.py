@@ -266,72 +266,209 @@ def time_kernels(moe, torch, d, steps, warmup):
 CACHE_FLUSH_BYTES = 512 << 20   # twice the 256 MB infinity cache
 
 
-def time_forward_cold(moe, torch, d, steps, warmup):
-    """Average of `steps` moe_forward calls, each bracketed by its own HIP
-    events, with the infinity cache evicted before each call by reading a
-    512 MB buffer (reads leave no dirty lines to write back during the call):
-    the layer's weights stream from HBM, as they do when every layer of a
-    model brings its own weights."""
-    sp = d["sp"]
-    shape = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
-    buf = moe.MoELayerBuffers(shape)
+def hwmon_dir(torch):
+    """The device's hwmon directory in sysfs (found by its PCI address), or None."""
+    import glob
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    except Exception:  # pragma: no cover
+        return None
+    dirs = sorted(glob.glob(f"/sys/bus/pci/devices/{bdf}/hwmon/hwmon*"))
+    return dirs[0] if dirs else None
+
+
+def read_hwmon(d) -> dict:
+    """Clock (MHz) and power (W) readings the hwmon directory exposes."""
+    def read(name):
+        try:
+            with open(os.path.join(d, name)) as f:
+                return f.read().strip()
+        except OSError:
+            return None
+    out = {}
+    for name in sorted(os.listdir(d)):
+        if name.startswith("freq") and name.endswith("_input"):
+            v = read(name)
+            label = read(name[:-len("_input")] + "_label") or name[:-len("_input")]
+            if v is not None and v.isdigit():
+                out[f"{label}_MHz"] = int(v) / 1e6
+        elif name.startswith("power") and name.endswith(("_input", "_average", "_cap")):
+            v = read(name)
+            if v is not None and v.isdigit():
+                out[f"{name}_W"] = int(v) / 1e6
+    return out
+
+
+def telemetry_during(torch, fn, calls):
+    """Median clock and power read from sysfs by the host while `calls`
+    back-to-back calls of `fn` run on the device (they are all enqueued first,
+    then the host samples until they finish)."""
+    d = hwmon_dir(torch)
+    if d is None:
+        return None
+    torch.cuda.synchronize()
+    done = torch.cuda.Event()
+    for _ in range(calls):
+        fn()
+    done.record()
+    samples = []
+    while not done.query():
+        samples.append(read_hwmon(d))
+        time.sleep(0.005)
+    torch.cuda.synchronize()
+    keys = sorted({k for smp in samples for k in smp})
+    res = {k: round(float(np.median([smp[k] for smp in samples if k in smp])), 1) for k in keys}
+    res.update({"samples": len(samples), "calls": calls, "source": f"{d} (sysfs, sampled every 5 ms)"})
+    return res
+
+
+def call_stats(ms_list) -> dict:
+    """Mean, median, min and 90th percentile of per-call times (ms)."""
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "min": round(float(a.min()), 5), "p90": round(float(np.percentile(a, 90)), 5), "calls": int(a.size)}
+
+
+def timed_cold(torch, fn, steps):
+    """Per-call HIP-event times of `fn` with the infinity cache evicted before
+    every call by reading a 512 MB buffer outside the event window (reads
+    leave no dirty lines to write back during the call)."""
     flush = torch.ones(CACHE_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in evs:
         torch.sum(flush, dim=0, out=sink)
         e0.record()
-        buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+        fn()
         e1.record()
     torch.cuda.synchronize()
     del flush
-    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])), buf
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def time_forward_cold(moe, torch, d, steps, warmup):
+    """Per-call times of `steps` moe_forward calls, the infinity cache
+    evicted before each: the layer's weights stream from HBM, as they do when
+    every layer of a model brings its own weights."""
+    sp = d["sp"]
+    shape = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
+    buf = moe.MoELayerBuffers(shape)
+    fwd = lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])  # noqa: E731
+    for _ in range(warmup):
+        fwd()
+    return timed_cold(torch, fwd, steps), buf
+
+
+def capture_forward(torch, buf, d):
+    """One moe_forward call captured as a HIP graph (through torch's graph
+    capture on a side stream, after eager warm-up calls on that stream)."""
+    fwd = lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])  # noqa: E731
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph_replay(moe, torch, d, steps, warmup, eager_out):
+    """The layer call replayed from a captured HIP graph (no per-kernel launch
+    work on the host), cold like the eager timing; the replayed output is
+    compared bit for bit with the eager call's."""
+    sp = d["sp"]
+    buf = moe.MoELayerBuffers(moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype))
+    g = capture_forward(torch, buf, d)
+    for _ in range(warmup):
+        g.replay()
+    ts = timed_cold(torch, g.replay, steps)
+    same = bool(torch.equal(buf.out.view(torch.int16), eager_out.view(torch.int16)))
+    del g
+    return ts, same
 
 
 def time_decode(moe, torch, steps, warmup):
     """The AR-decode layer (T=8): moe_forward time and algorithmic GB/s, with
-    the weights streamed from HBM (cache evicted before every call), and the
-    same back to back (part of the active weights then stays in the 256 MB
-    infinity cache between calls; labelled warm_cache)."""
+    the weights streamed from HBM (cache evicted before every call); the same
+    call replayed from a captured HIP graph; and the eager call back to back
+    (part of the active weights then stays in the 256 MB infinity cache
+    between calls; labelled warm_cache)."""
     sp3 = mi.spec("decode")
     d3 = upload(mi.make_layer(sp3), torch)
-    ms3, b3 = time_forward_cold(moe, torch, d3, steps, warmup)
+    ts, b3 = time_forward_cold(moe, torch, d3, steps, warmup)
+    ms3 = float(np.mean(ts))
+    gts, same = time_graph_replay(moe, torch, d3, steps, warmup, b3.out)
+    ms_graph = float(np.mean(gts))
     ms_warm, _, _ = time_forward(moe, torch, d3, steps, warmup)
     n_active = int((b3.views()["counts"].cpu().numpy() > 0).sum())
     nbytes = decode_bytes(sp3, n_active)
-    gbs = nbytes / (ms3 * 1e-3) / 1e9
-    gbs_warm = nbytes / (ms_warm * 1e-3) / 1e9
-    return {"ms": round(ms3, 5), "GB_per_s": round(gbs, 1),
-            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "active_experts": n_active,
-            "algorithmic_bytes": nbytes, "cache": "evicted before every call",
-            "warm_cache": {"ms": round(ms_warm, 5), "GB_per_s": round(gbs_warm, 1),
-                           "frac_of_hbm_peak": round(gbs_warm / PEAK_HBM_GBS, 4)}}
+    rate = lambda ms: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
+    return {"ms": round(ms3, 5), "GB_per_s": round(rate(ms3), 1),
+            "frac_of_hbm_peak": round(rate(ms3) / PEAK_HBM_GBS, 4), "active_experts": n_active,
+            "algorithmic_bytes": nbytes, "cache": "evicted before every call", "per_call_ms": call_stats(ts),
+            "graph_replay": {"ms": round(ms_graph, 5), "GB_per_s": round(rate(ms_graph), 1),
+                             "frac_of_hbm_peak": round(rate(ms_graph) / PEAK_HBM_GBS, 4),
+                             "per_call_ms": call_stats(gts), "output_equals_eager": same,
+                             "cache": "evicted before every replay"},
+            "warm_cache": {"ms": round(ms_warm, 5), "GB_per_s": round(rate(ms_warm), 1),
+                           "frac_of_hbm_peak": round(rate(ms_warm) / PEAK_HBM_GBS, 4)}}
 
 
-def cpu_baseline(base, n_tokens: int):
-    """The oracle as it stands, on the first n_tokens tokens of the layer."""
+def host_description() -> dict:
+    """CPU model and the BLAS library numpy's float32 GEMMs run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = {"library": libs[0].get("internal_api"), "version": libs[0].get("version"),
+                    "threads": libs[0].get("num_threads")}
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
+def cpu_baseline(base, n_tokens: int, runs: int = 3):
+    """The oracle as it stands, on the first n_tokens tokens of the layer:
+    one warm-up call, then the median of `runs` timed calls."""
     import dataclasses
 
     import oracle as o
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    host = host_description()
+    threads = (host["blas"] or {}).get("threads") or len(os.sched_getaffinity(0))
     sp = dataclasses.replace(base.spec, T=n_tokens)
     inp = mi.LayerInputs(sp, base.x[:n_tokens], base.wg, base.bias, base.w1, base.w2)
-    t0 = time.perf_counter()
     o.forward(inp)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        o.forward(inp)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     return {
         "value": round(expert_flops(sp) / dt / 1e12, 6), "unit": "TFLOP/s",
-        "tokens_per_s": round(n_tokens / dt, 2), "seconds": round(dt, 2), "cores": int(threads),
+        "tokens_per_s": round(n_tokens / dt, 2), "seconds": round(dt, 2),
+        "seconds_each": [round(t, 2) for t in times], "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"oracle forward (fp64 numpy, full routing + all {sp.E} experts) on "
+        "sample": (f"oracle forward (fp64 numpy: router, permutation, all {sp.E} experts' GEMMs through BLAS, finalize) on "
                    + (f"the whole layer ({n_tokens} tokens)" if n_tokens >= base.spec.T else
-                      f"the first {n_tokens} of {base.spec.T} tokens of the same layer")),
+                      f"the first {n_tokens} of {base.spec.T} tokens of the same layer")
+                   + f"; median of {runs} timed calls after one warm-up call"),
+        "host": host,
     }
 
 
@@ -384,6 +521,9 @@ def main(argv=None):
     log("timing moe_forward")
     ms, wall_ms, buf = time_forward(moe, torch, d, args.steps, args.warmup)
     log(f"layer {ms:.4f} ms/step (wall {wall_ms:.4f})")
+    tele = telemetry_during(torch, lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"]), 300)
+    if tele is not None:
+        log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith(("_MHz", "_W"))))
     kern, counts = time_kernels(moe, torch, d, args.steps, args.warmup)
     log("kernels " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in kern.items()))
 
@@ -417,6 +557,7 @@ def main(argv=None):
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "down_gemm_tflops": round(down_tf, 2),
         "expert_loads": {"min": int(counts.min()), "max": int(counts.max())},
+        "telemetry_during_layer": tele,
     }
     del buf
 
@@ -450,7 +591,11 @@ def main(argv=None):
                                "tokens_per_s": round(sp4.T / (ms4 * 1e-3), 1),
                                "max_load": int(c4.max()), "empty_experts": int((c4 == 0).sum())}
         log(f"skewed {ms4:.4f} ms")
-        del d2, d4, b4buf
+        del b4buf
+        extra["skewed_cfg"]["two_dispatch_ablation"] = time_two_dispatch(
+            moe, torch, d4, max(3, args.steps // 2), args.warmup, ms4)
+        log(f"skewed two-dispatch {extra['skewed_cfg']['two_dispatch_ablation']['ms_two_dispatch']:.4f} ms")
+        del d2, d4
         torch.cuda.empty_cache()
         extra["decode"] = decode
         res["other_layers"] = extra
