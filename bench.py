@@ -392,6 +392,40 @@ def time_graph_replay(moe, torch, d, steps, warmup, eager_out):
     return ts, same
 
 
+def shared_flops(sp, Is) -> float:
+    """The shared expert's FLOPs: gate|up (4*T*H*Is) and down (2*T*Is*H)."""
+    return 6.0 * sp.T * sp.H * Is
+
+
+def time_shared(moe, torch, d, steps, warmup, cold=False):
+    """The layer with its shared expert (moe_forward_shared, width = the
+    routed shard's I): per-call times, cold (cache evicted before each call)
+    or back to back, and the shared expert's bytes of weights."""
+    sp = d["sp"]
+    w1s, w2s = mi.make_shared(sp)
+    Is = w2s.shape[1]
+    dw1s, dw2s = dev(w1s, torch), dev(w2s, torch)
+    shape = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
+    buf = moe.MoELayerBuffers(shape, shared_Im=Is)
+    fwd = lambda: buf.forward_shared(d["x"], d["wg"], d["bias"], d["w1"], d["w2"], dw1s, dw2s)  # noqa: E731
+    for _ in range(warmup):
+        fwd()
+    if cold:
+        ts = timed_cold(torch, fwd, steps)
+    else:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fwd()
+        e1.record()
+        torch.cuda.synchronize()
+        ts = [e0.elapsed_time(e1) / steps]
+    n_active = int((buf.views()["counts"].cpu().numpy() > 0).sum())
+    del buf, dw1s, dw2s
+    return float(np.mean(ts)), Is, n_active, (3 * Is * sp.H * (2 if sp.dtype == mi.BF16 else 4))
+
+
 def time_decode(moe, torch, steps, warmup):
     """The AR-decode layer (T=8): moe_forward time and algorithmic GB/s, with
     the weights streamed from HBM (cache evicted before every call); the same
@@ -408,6 +442,8 @@ def time_decode(moe, torch, steps, warmup):
     n_active = int((b3.views()["counts"].cpu().numpy() > 0).sum())
     nbytes = decode_bytes(sp3, n_active)
     rate = lambda ms: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
+    ms_sh, Is, _, sh_bytes = time_shared(moe, torch, d3, steps, warmup, cold=True)
+    sh_rate = (nbytes + sh_bytes) / (ms_sh * 1e-3) / 1e9
     return {"ms": round(ms3, 5), "GB_per_s": round(rate(ms3), 1),
             "frac_of_hbm_peak": round(rate(ms3) / PEAK_HBM_GBS, 4), "active_experts": n_active,
             "algorithmic_bytes": nbytes, "cache": "evicted before every call", "per_call_ms": call_stats(ts),
@@ -416,7 +452,10 @@ def time_decode(moe, torch, steps, warmup):
                              "per_call_ms": call_stats(gts), "output_equals_eager": same,
                              "cache": "evicted before every replay"},
             "warm_cache": {"ms": round(ms_warm, 5), "GB_per_s": round(rate(ms_warm), 1),
-                           "frac_of_hbm_peak": round(rate(ms_warm) / PEAK_HBM_GBS, 4)}}
+                           "frac_of_hbm_peak": round(rate(ms_warm) / PEAK_HBM_GBS, 4)},
+            "with_shared_expert": {"ms": round(ms_sh, 5), "shared_Im": Is, "shared_weight_bytes": sh_bytes,
+                                   "GB_per_s": round(sh_rate, 1), "frac_of_hbm_peak": round(sh_rate / PEAK_HBM_GBS, 4),
+                                   "added_ms": round(ms_sh - ms3, 5), "cache": "evicted before every call"}}
 
 
 def host_description() -> dict:
@@ -525,6 +564,14 @@ def main(argv=None):
     if tele is not None:
         log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith(("_MHz", "_W"))))
     kern, counts = time_kernels(moe, torch, d, args.steps, args.warmup)
+    shared = None
+    if not args.no_extra:
+        ms_sh, Is, _, _ = time_shared(moe, torch, d, args.steps, args.warmup)
+        fl = expert_flops(sp) + shared_flops(sp, Is)
+        shared = {"ms": round(ms_sh, 4), "shared_Im": Is, "tflops": round(fl / (ms_sh * 1e-3) / 1e12, 2),
+                  "tokens_per_s": round(sp.T / (ms_sh * 1e-3), 1), "added_ms": round(ms_sh - ms, 4),
+                  "shared_tflops": round(shared_flops(sp, Is) / ((ms_sh - ms) * 1e-3) / 1e12, 2)}
+        log(f"with shared expert {ms_sh:.4f} ms")
     log("kernels " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in kern.items()))
 
     flops = expert_flops(sp)
@@ -562,7 +609,7 @@ def main(argv=None):
     del buf
 
     if not args.no_extra:
-        extra = {}
+        extra = {"denoise_with_shared_expert": shared}
         # 2-micro denoise (same weights, micro-major)
         sp2 = mi.spec("denoise_2micro")
         w1, w2 = relayout_two_micro(base, sp2)

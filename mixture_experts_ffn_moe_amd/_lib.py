@@ -24,6 +24,9 @@ EXPORTED = (
     "moe_status_string", "moe_workspace_size", "moe_get_workspace_layout", "moe_route",
     "moe_permute", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_down", "moe_finalize",
     "moe_forward",
+    # shared expert (moe_shared.h)
+    "moe_shared_workspace_size", "moe_get_shared_workspace_layout", "moe_shared_ffn",
+    "moe_finalize_shared", "moe_forward_shared",
     # measurement probes (moe_probe.h)
     "moe_probe_mfma_bf16", "moe_probe_mfma_flops", "moe_probe_read",
 )
@@ -45,6 +48,10 @@ class MoeWorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("logits", "topk_ids", "topk_w", "counts", "offsets", "perm", "inv", "h", "y",
                  "scratch", "total")]
+
+
+class MoeSharedLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("hs", "ys", "total")]
 
 
 def _load():
@@ -72,6 +79,16 @@ def _load():
     lib.moe_finalize.restype = i32
     lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_forward.restype = i32
+    lib.moe_shared_workspace_size.argtypes = [S, i32]
+    lib.moe_shared_workspace_size.restype = ctypes.c_size_t
+    lib.moe_get_shared_workspace_layout.argtypes = [S, i32, ctypes.POINTER(MoeSharedLayout)]
+    lib.moe_get_shared_workspace_layout.restype = i32
+    lib.moe_shared_ffn.argtypes = [S, i32, P, P, P, P, P, P]
+    lib.moe_shared_ffn.restype = i32
+    lib.moe_finalize_shared.argtypes = [S, P, P, P, P, P, P]
+    lib.moe_finalize_shared.restype = i32
+    lib.moe_forward_shared.argtypes = [S, i32, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_forward_shared.restype = i32
     lib.moe_probe_mfma_bf16.argtypes = [i32, P, P]
     lib.moe_probe_mfma_bf16.restype = i32
     lib.moe_probe_mfma_flops.argtypes = [i32]
@@ -198,20 +215,65 @@ def moe_finalize(shape, y, inv, topk_w, out, stream=None):
                             _stream(stream)), "moe_finalize")
 
 
+def _workspace(workspace):
+    if workspace is None:
+        raise ValueError("workspace: a tensor is required")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous GPU tensor")
+    return _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size())
+
+
 def moe_forward(shape, x, wg, bias, w1, w2, out, workspace, stream=None):
     T, H, E, Im, mu = shape.T, shape.H, shape.E, shape.Im, shape.micro_count
     dt = _layer_dtype(shape)
-    if workspace is None:
-        raise ValueError("workspace: a tensor is required")
-    if workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace: must be a contiguous GPU tensor")
-    nbytes = workspace.numel() * workspace.element_size()
+    ws, nbytes = _workspace(workspace)
     _check(lib.moe_forward(ctypes.byref(shape), _arg("x", x, dt, T * H), _arg("wg", wg, torch.float32, E * H),
                            _arg("gate_bias", bias, torch.float32, E, nullable=True),
                            _arg("w1", w1, dt, mu * E * 2 * Im * H), _arg("w2", w2, dt, mu * E * H * Im),
-                           _arg("out", out, dt, T * H), _ptr(workspace), ctypes.c_size_t(nbytes),
-                           _stream(stream)),
+                           _arg("out", out, dt, T * H), ws, nbytes, _stream(stream)),
            "moe_forward")
+
+
+def moe_shared_workspace_size(shape: MoeShape, Is: int) -> int:
+    return int(lib.moe_shared_workspace_size(ctypes.byref(shape), int(Is)))
+
+
+def moe_get_shared_workspace_layout(shape: MoeShape, Is: int) -> dict:
+    L = MoeSharedLayout()
+    _check(lib.moe_get_shared_workspace_layout(ctypes.byref(shape), int(Is), ctypes.byref(L)),
+           "moe_get_shared_workspace_layout")
+    return {n: int(getattr(L, n)) for n, _ in MoeSharedLayout._fields_}
+
+
+def moe_shared_ffn(shape, Is, x, w1s, w2s, hs, ys, stream=None):
+    T, H = shape.T, shape.H
+    dt = _layer_dtype(shape)
+    _check(lib.moe_shared_ffn(ctypes.byref(shape), int(Is), _arg("x", x, dt, T * H),
+                              _arg("w1s", w1s, dt, 2 * Is * H), _arg("w2s", w2s, dt, H * Is),
+                              _arg("hs", hs, dt, T * Is), _arg("ys", ys, dt, T * H), _stream(stream)),
+           "moe_shared_ffn")
+
+
+def moe_finalize_shared(shape, y, inv, topk_w, ys, out, stream=None):
+    T, H, k = shape.T, shape.H, shape.k
+    R = T * k
+    dt = _layer_dtype(shape)
+    _check(lib.moe_finalize_shared(ctypes.byref(shape), _arg("y", y, dt, R * H), _arg("inv", inv, torch.int32, R),
+                                   _arg("topk_w", topk_w, torch.float32, R), _arg("ys", ys, dt, T * H),
+                                   _arg("out", out, dt, T * H), _stream(stream)), "moe_finalize_shared")
+
+
+def moe_forward_shared(shape, Is, x, wg, bias, w1, w2, w1s, w2s, out, workspace, stream=None):
+    T, H, E, Im, mu = shape.T, shape.H, shape.E, shape.Im, shape.micro_count
+    dt = _layer_dtype(shape)
+    ws, nbytes = _workspace(workspace)
+    _check(lib.moe_forward_shared(ctypes.byref(shape), int(Is), _arg("x", x, dt, T * H),
+                                  _arg("wg", wg, torch.float32, E * H),
+                                  _arg("gate_bias", bias, torch.float32, E, nullable=True),
+                                  _arg("w1", w1, dt, mu * E * 2 * Im * H), _arg("w2", w2, dt, mu * E * H * Im),
+                                  _arg("w1s", w1s, dt, 2 * Is * H), _arg("w2s", w2s, dt, H * Is),
+                                  _arg("out", out, dt, T * H), ws, nbytes, _stream(stream)),
+           "moe_forward_shared")
 
 
 def moe_probe_mfma_bf16(iterations: int, sink, stream=None) -> float:

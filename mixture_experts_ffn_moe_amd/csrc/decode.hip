@@ -14,11 +14,12 @@
 //      bias, one fp32 rounding, top-k and weights (same rules as route.hip),
 //      expert counts and offsets, the stable permutation and its inverse, and
 //      the ascending list of active experts.
-//   3. decode_w13: one workgroup per (active expert, 64 columns of the
-//      micro-major intermediate); each wave streams 16 gate and 16 up rows of
-//      w1 in whole 128-byte lines, re-lays them through LDS into MFMA B
-//      fragments (M = the expert's rows, padded to 16) and applies SwiGLU; h
-//      is rounded to bf16.
+//   3. decode_w13: one wave per (active expert, 16 columns of the
+//      micro-major intermediate), the waves' units dealt evenly over one
+//      workgroup per CU; each wave streams 16 gate and 16 up rows of w1 in
+//      whole 128-byte lines, re-lays them through LDS into MFMA B fragments
+//      (M = the expert's rows, padded to 16) and applies SwiGLU; h is rounded
+//      to bf16.
 //   4. decode_down_finalize: one workgroup per 16 output columns; its eight
 //      waves split the active experts (enough loads in flight per CU), stream
 //      the matching w2 rows the same way, and put
@@ -26,6 +27,11 @@
 //      summed in ascending j (the finalize of section 6.1), so the down
 //      partials of every micro-shard and route are reduced once, without
 //      atomics and without a y tensor.
+// With a shared expert ("HunyuanImage-3.0 on CANN NPU", section 3.1) its
+// weights stream in the same two launches: decode_w13 runs its gate|up
+// columns for every token as extra units of its work list, and
+// decode_down_finalize takes it as one more work item whose per-token slot
+// (weight 1) is added after the routed sum.
 #include "moe_common.h"
 
 namespace moe {
@@ -249,75 +255,113 @@ struct WaveRows {
 };
 
 // ---------------------------------------------------------------------------
-// 3. gate|up + SwiGLU for one active expert and 64 intermediate columns.
-__global__ __launch_bounds__(256) void decode_w13(const uint16_t* __restrict__ x,
-                                                  const int32_t* __restrict__ perm,
-                                                  const int32_t* __restrict__ offsets,
-                                                  const int32_t* __restrict__ active,
-                                                  const uint16_t* __restrict__ w1, int H, int E,
-                                                  int k, int Im, int mu, int ncg,
-                                                  uint16_t* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) char buf[4][2][2048];  // per wave: gate, up
-  const int a = blockIdx.x / ncg, cg = blockIdx.x % ncg;
-  if (a >= active[kMaxExperts]) return;
-  const int e = active[a];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seg = offsets[e], n = offsets[e + 1] - seg;
-  const int c0 = cg * 64 + wave * 16;      // column in [0, mu*Im)
-  const int micro = c0 / Im, i0 = c0 - micro * Im;
+// 3. gate|up + SwiGLU.  The work is a list of units, one per (active expert,
+// 16 intermediate columns) and then one per 16 columns of the shared expert;
+// a unit is one wave's stream of 16 gate and 16 up rows over all of H.  Each
+// of the kW13Blocks workgroups takes an equal contiguous share of the list
+// (the list length is known only on the device), its waves taking the share's
+// units in turn: every CU streams the same number of bytes (to one unit),
+// whatever the number of active experts.  (With one workgroup per 4 units, a 43rd active expert or a shared
+// expert put three workgroups on some CUs, and those CUs, served the same
+// share of HBM bandwidth as the rest, finished ~25% later.)
+constexpr int kW13Waves = 16;    // waves per workgroup; a wave takes every 16th unit of its share
+constexpr int kW13Blocks = 256;  // one workgroup per CU
+
+__global__ __launch_bounds__(kW13Waves * 64) void decode_w13(const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ perm,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ active,
+                                                           const uint16_t* __restrict__ w1, int T,
+                                                           int H, int E, int k, int Im, int mu,
+                                                           uint16_t* __restrict__ h,
+                                                           const uint16_t* __restrict__ w1s, int Is,
+                                                           uint16_t* __restrict__ hs) {
+  __shared__ __attribute__((aligned(16))) char buf[kW13Waves][2][2048];  // per wave: gate, up
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  const WaveRows wr(lane);
-  char* gb = buf[wave][0];
-  char* ub = buf[wave][1];
-
-  const bool row_ok = fr < n;
-  const uint16_t* arow = x + (size_t)(perm[seg + min(fr, n - 1)] / k) * H + fk;
-  const uint16_t* wbase = w1 + (size_t)(micro * E + e) * 2 * Im * H;
-  // rows lane/8 and 8 + lane/8 of the gate and up blocks, chunk lane % 8
-  const uint16_t* g0 = wbase + (size_t)(i0 + (lane >> 3)) * H + (lane & 7) * 8;
-  const uint16_t* u0 = wbase + (size_t)(Im + i0 + (lane >> 3)) * H + (lane & 7) * 8;
-  const size_t r8 = (size_t)8 * H;
-
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < H; k0 += kStep * kStepsW13) {
-    uint4 gv[kStepsW13][2], uv[kStepsW13][2], av[kStepsW13][2];
-#pragma unroll
-    for (int q = 0; q < kStepsW13; ++q) {
-      const int kk = k0 + kStep * q;
-      gv[q][0] = *reinterpret_cast<const uint4*>(g0 + kk);
-      gv[q][1] = *reinterpret_cast<const uint4*>(g0 + r8 + kk);
-      uv[q][0] = *reinterpret_cast<const uint4*>(u0 + kk);
-      uv[q][1] = *reinterpret_cast<const uint4*>(u0 + r8 + kk);
-      av[q][0] = *reinterpret_cast<const uint4*>(arow + kk);
-      av[q][1] = *reinterpret_cast<const uint4*>(arow + kk + 32);
+  const int ue = mu * Im / 16;                      // units per routed expert
+  const int routed_units = active[kMaxExperts] * ue;
+  const int units = routed_units + (w1s != nullptr ? Is / 16 : 0);
+  const int u_end = (int)((long long)(blockIdx.x + 1) * units / gridDim.x);
+  for (int u = (int)((long long)blockIdx.x * units / gridDim.x) + wave; u < u_end; u += kW13Waves) {
+    int n, c0, i0, Imx, ldh;
+    const uint16_t* arow;
+    const uint16_t* wbase;
+    uint16_t* hout;
+    if (u >= routed_units) {
+      // shared expert: every token, in order
+      n = T;
+      c0 = (u - routed_units) * 16;
+      i0 = c0;
+      Imx = Is;
+      ldh = Is;
+      arow = x + (size_t)min(fr, n - 1) * H + fk;
+      wbase = w1s;
+      hout = hs;
+    } else {
+      const int e = active[u / ue];
+      const int seg = offsets[e];
+      n = offsets[e + 1] - seg;
+      c0 = (u % ue) * 16;  // column in [0, mu*Im)
+      const int micro = c0 / Im;
+      i0 = c0 - micro * Im;
+      Imx = Im;
+      ldh = mu * Im;
+      arow = x + (size_t)(perm[seg + min(fr, n - 1)] / k) * H + fk;
+      wbase = w1 + (size_t)(micro * E + e) * 2 * Im * H;
+      hout = h + (size_t)seg * ldh;
     }
+    const WaveRows wr(lane);
+    char* gb = buf[wave][0];
+    char* ub = buf[wave][1];
+
+    const bool row_ok = fr < n;
+    // rows lane/8 and 8 + lane/8 of the gate and up blocks, chunk lane % 8
+    const uint16_t* g0 = wbase + (size_t)(i0 + (lane >> 3)) * H + (lane & 7) * 8;
+    const uint16_t* u0 = wbase + (size_t)(Imx + i0 + (lane >> 3)) * H + (lane & 7) * 8;
+    const size_t r8 = (size_t)8 * H;
+
+    f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < H; k0 += kStep * kStepsW13) {
+      uint4 gv[kStepsW13][2], uv[kStepsW13][2], av[kStepsW13][2];
 #pragma unroll
-    for (int q = 0; q < kStepsW13; ++q) {
-      *reinterpret_cast<uint4*>(gb + wr.wr0) = gv[q][0];
-      *reinterpret_cast<uint4*>(gb + wr.wr1) = gv[q][1];
-      *reinterpret_cast<uint4*>(ub + wr.wr0) = uv[q][0];
-      *reinterpret_cast<uint4*>(ub + wr.wr1) = uv[q][1];
-      const uint4 gf0 = *reinterpret_cast<const uint4*>(gb + wr.rd0);
-      const uint4 gf1 = *reinterpret_cast<const uint4*>(gb + wr.rd1);
-      const uint4 uf0 = *reinterpret_cast<const uint4*>(ub + wr.rd0);
-      const uint4 uf1 = *reinterpret_cast<const uint4*>(ub + wr.rd1);
-      uint4 a0 = av[q][0], a1 = av[q][1];
-      if (!row_ok) a0 = a1 = make_uint4(0, 0, 0, 0);
-      const bf16x8 A0 = __builtin_bit_cast(bf16x8, a0), A1 = __builtin_bit_cast(bf16x8, a1);
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, gf0), accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, uf0), accu, 0, 0, 0);
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, gf1), accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, uf1), accu, 0, 0, 0);
+      for (int q = 0; q < kStepsW13; ++q) {
+        const int kk = k0 + kStep * q;
+        gv[q][0] = *reinterpret_cast<const uint4*>(g0 + kk);
+        gv[q][1] = *reinterpret_cast<const uint4*>(g0 + r8 + kk);
+        uv[q][0] = *reinterpret_cast<const uint4*>(u0 + kk);
+        uv[q][1] = *reinterpret_cast<const uint4*>(u0 + r8 + kk);
+        av[q][0] = *reinterpret_cast<const uint4*>(arow + kk);
+        av[q][1] = *reinterpret_cast<const uint4*>(arow + kk + 32);
+      }
+#pragma unroll
+      for (int q = 0; q < kStepsW13; ++q) {
+        *reinterpret_cast<uint4*>(gb + wr.wr0) = gv[q][0];
+        *reinterpret_cast<uint4*>(gb + wr.wr1) = gv[q][1];
+        *reinterpret_cast<uint4*>(ub + wr.wr0) = uv[q][0];
+        *reinterpret_cast<uint4*>(ub + wr.wr1) = uv[q][1];
+        const uint4 gf0 = *reinterpret_cast<const uint4*>(gb + wr.rd0);
+        const uint4 gf1 = *reinterpret_cast<const uint4*>(gb + wr.rd1);
+        const uint4 uf0 = *reinterpret_cast<const uint4*>(ub + wr.rd0);
+        const uint4 uf1 = *reinterpret_cast<const uint4*>(ub + wr.rd1);
+        uint4 a0 = av[q][0], a1 = av[q][1];
+        if (!row_ok) a0 = a1 = make_uint4(0, 0, 0, 0);
+        const bf16x8 A0 = __builtin_bit_cast(bf16x8, a0), A1 = __builtin_bit_cast(bf16x8, a1);
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, gf0), accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, uf0), accu, 0, 0, 0);
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, gf1), accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, uf1), accu, 0, 0, 0);
+      }
     }
-  }
-  // D layout: register r holds row 4*(lane/16) + r, column lane%16
-  const int ldh = mu * Im;
+    // D layout: register r holds row 4*(lane/16) + r, column lane%16
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * (lane >> 4) + r;
-    if (row < n)
-      h[(size_t)(seg + row) * ldh + c0 + fr] = float_to_bf16_bits(silu_f32(accg[r]) * accu[r]);
-  }
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * (lane >> 4) + r;
+      if (row < n)
+        hout[(size_t)row * ldh + c0 + fr] = float_to_bf16_bits(silu_f32(accg[r]) * accu[r]);
+    }
+  }  // units of this wave
 }
 
 // ---------------------------------------------------------------------------
@@ -326,33 +370,54 @@ __global__ __launch_bounds__(kDownWaves * 64) void decode_down_finalize(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const float* __restrict__ topw, const uint16_t* __restrict__ w2, int T, int H, int E, int k,
-    int Im, int mu, uint16_t* __restrict__ out) {
+    int Im, int mu, uint16_t* __restrict__ out, const uint16_t* __restrict__ hs,
+    const uint16_t* __restrict__ w2s, int Is) {
   __shared__ float slot[kDecT * kMaxK][16];
+  __shared__ float sslot[kDecT][16];  // the shared expert's output, per token
   __shared__ __attribute__((aligned(16))) char buf[kDownWaves][2048];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   const int n_act = active[kMaxExperts];
-  const int K = mu * Im;
+  const bool has_shared = hs != nullptr;
+  const int n_items = n_act + (has_shared ? 1 : 0);  // item n_act is the shared expert
   const WaveRows wr(lane);
   char* wb = buf[wave];
-  const size_t r8 = (size_t)8 * Im;
 
-  for (int a = wave; a < n_act; a += kDownWaves) {
-    const int e = active[a];
-    const int seg = offsets[e], n = offsets[e + 1] - seg;
+  for (int a = wave; a < n_items; a += kDownWaves) {
+    const bool sh = a == n_act;
+    int n, K, Imx, seg = 0;
+    size_t mstride;
+    const uint16_t* arow;
+    const uint16_t* b0;
+    // rows n0 + lane/8 and n0 + 8 + lane/8 of the down weights, chunk lane % 8
+    if (sh) {
+      n = T;
+      K = Is;
+      Imx = Is;
+      mstride = 0;
+      arow = hs + (size_t)min(fr, n - 1) * Is + fk;
+      b0 = w2s + (size_t)(n0 + (lane >> 3)) * Is + (lane & 7) * 8;
+    } else {
+      const int e = active[a];
+      seg = offsets[e];
+      n = offsets[e + 1] - seg;
+      K = mu * Im;
+      Imx = Im;
+      mstride = (size_t)E * H * Im;
+      arow = h + (size_t)(seg + min(fr, n - 1)) * K + fk;
+      b0 = w2 + ((size_t)e * H + n0 + (lane >> 3)) * Im + (lane & 7) * 8;
+    }
     const bool row_ok = fr < n;
-    const uint16_t* arow = h + (size_t)(seg + min(fr, n - 1)) * K + fk;
-    // rows n0 + lane/8 and n0 + 8 + lane/8 of w2[.][e], chunk lane % 8
-    const uint16_t* b0 = w2 + ((size_t)e * H + n0 + (lane >> 3)) * Im + (lane & 7) * 8;
+    const size_t r8 = (size_t)8 * Imx;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < K; k0 += kStep * kStepsDown) {
       uint4 bv[kStepsDown][2], av[kStepsDown][2];
 #pragma unroll
       for (int q = 0; q < kStepsDown; ++q) {
         const int kg = k0 + kStep * q;  // a 64-step never crosses a micro boundary (Im % 256 == 0)
-        const int mm = kg / Im;
-        const uint16_t* bp = b0 + (size_t)mm * E * H * Im + (kg - mm * Im);
+        const int mm = kg / Imx;
+        const uint16_t* bp = b0 + (size_t)mm * mstride + (kg - mm * Imx);
         bv[q][0] = *reinterpret_cast<const uint4*>(bp);
         bv[q][1] = *reinterpret_cast<const uint4*>(bp + r8);
         av[q][0] = *reinterpret_cast<const uint4*>(arow + kg);
@@ -376,17 +441,23 @@ __global__ __launch_bounds__(kDownWaves * 64) void decode_down_finalize(
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * (lane >> 4) + r;
       if (row < n) {
-        const int route = perm[seg + row];  // = t * k + j
-        slot[route][fr] = topw[route] * acc[r];
+        if (sh) {
+          sslot[row][fr] = acc[r];
+        } else {
+          const int route = perm[seg + row];  // = t * k + j
+          slot[route][fr] = topw[route] * acc[r];
+        }
       }
     }
   }
   __syncthreads();
-  // out[t, n0 + c] = sum over j ascending of the route slots
+  // out[t, n0 + c] = sum over j ascending of the route slots, then the shared
+  // expert's slot
   for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
     const int t = i >> 4, c = i & 15;
     float s = 0.0f;
     for (int j = 0; j < k; ++j) s += slot[t * k + j][c];
+    if (has_shared) s += sslot[t][c];
     out[(size_t)t * H + n0 + c] = float_to_bf16_bits(s);
   }
 }
@@ -395,6 +466,10 @@ __global__ __launch_bounds__(kDownWaves * 64) void decode_down_finalize(
 
 size_t decode_scratch_bytes() {
   return (size_t)kSplit * kDecT * kMaxExperts * sizeof(double) + (kMaxExperts + 1) * sizeof(int32_t);
+}
+
+bool decode_shared_supported(int Is) {
+  return Is > 0 && (Is % 64) == 0 && (Is % (kStep * kStepsDown)) == 0;
 }
 
 bool decode_supported(const Shape& s) {
@@ -406,20 +481,23 @@ bool decode_supported(const Shape& s) {
 hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const float* bias,
                          const void* w1, const void* w2, void* out, float* logits, int32_t* ids,
                          float* w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                         void* h, void* scratch, hipStream_t st) {
+                         void* h, void* scratch, hipStream_t st, const SharedExpert* shared) {
   double* partial = (double*)scratch;
   int32_t* active = (int32_t*)((char*)scratch + (size_t)kSplit * kDecT * kMaxExperts * sizeof(double));
   hipLaunchKernelGGL(decode_route_partial, dim3(kSplit), dim3(256), 0, st, (const uint16_t*)x, wg,
                      s.T, s.H, s.E, partial);
   hipLaunchKernelGGL(decode_route_finish, dim3(1), dim3(1024), 0, st, partial, bias, s.T, s.E,
                      s.k, logits, ids, w, counts, offsets, perm, inv, active);
-  const int ncg = s.mu * s.Im / 64;
-  hipLaunchKernelGGL(decode_w13, dim3(s.E * ncg), dim3(256), 0, st, (const uint16_t*)x, perm,
-                     offsets, active, (const uint16_t*)w1, s.H, s.E, s.k, s.Im, s.mu, ncg,
-                     (uint16_t*)h);
+  const uint16_t* w1s = shared ? (const uint16_t*)shared->w1 : nullptr;
+  const uint16_t* w2s = shared ? (const uint16_t*)shared->w2 : nullptr;
+  uint16_t* hs = shared ? (uint16_t*)shared->h : nullptr;
+  const int Is = shared ? shared->Is : 0;
+  hipLaunchKernelGGL(decode_w13, dim3(kW13Blocks), dim3(kW13Waves * 64), 0, st, (const uint16_t*)x,
+                     perm, offsets, active, (const uint16_t*)w1, s.T, s.H, s.E, s.k, s.Im, s.mu,
+                     (uint16_t*)h, w1s, Is, hs);
   hipLaunchKernelGGL(decode_down_finalize, dim3(s.H / 16), dim3(kDownWaves * 64), 0, st, (const uint16_t*)h,
                      perm, offsets, active, w, (const uint16_t*)w2, s.T, s.H, s.E, s.k, s.Im,
-                     s.mu, (uint16_t*)out);
+                     s.mu, (uint16_t*)out, (const uint16_t*)hs, w2s, Is);
   return hipGetLastError();
 }
 

@@ -7,7 +7,10 @@
 // accumulator, so each route contributes one row of y.
 //
 // out[t, :] = sum_{j ascending} w[t, j] * y[inv[t*k + j], :] in fp32, one
-// rounding.  No atomics: every output element is owned by one thread, so the
+// rounding.  With a shared expert ("HunyuanImage-3.0 on CANN NPU", section
+// 3.1: every token also passes through a shared expert whose output joins the
+// routed experts' sum) its output row ys[t, :] is added after the routed sum,
+// before the rounding.  No atomics: every output element is owned by one thread, so the
 // result is bitwise reproducible.  One workgroup per token; each thread moves
 // 16-byte vectors, so every row read is fully coalesced.
 #include "moe_common.h"
@@ -18,7 +21,8 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ y,
                                                        const int32_t* __restrict__ inv,
-                                                       const float* __restrict__ w, int H, int k,
+                                                       const float* __restrict__ w,
+                                                       const T* __restrict__ ys, int H, int k,
                                                        T* __restrict__ out) {
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
   const int t = blockIdx.x;
@@ -36,6 +40,12 @@ __global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ y,
 #pragma unroll
       for (int q = 0; q < V; ++q) acc[q] = fmaf(s, Elem<T>::to_f(v[q]), acc[q]);
     }
+    if (ys != nullptr) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(ys + (size_t)t * H + c);
+      const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] += Elem<T>::to_f(v[q]);
+    }
     uint4 res;
     T* o = reinterpret_cast<T*>(&res);
 #pragma unroll
@@ -47,13 +57,13 @@ __global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ y,
 }  // namespace
 
 hipError_t launch_finalize(const Shape& s, const void* y, const int32_t* inv, const float* w,
-                           void* out, hipStream_t st) {
+                           void* out, hipStream_t st, const void* ys) {
   if (s.bf16)
     hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3(s.T), dim3(256), 0, st,
-                       (const uint16_t*)y, inv, w, s.H, s.k, (uint16_t*)out);
+                       (const uint16_t*)y, inv, w, (const uint16_t*)ys, s.H, s.k, (uint16_t*)out);
   else
     hipLaunchKernelGGL(finalize_kernel<float>, dim3(s.T), dim3(256), 0, st, (const float*)y, inv,
-                       w, s.H, s.k, (float*)out);
+                       w, (const float*)ys, s.H, s.k, (float*)out);
   return hipGetLastError();
 }
 

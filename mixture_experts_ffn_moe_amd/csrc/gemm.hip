@@ -41,11 +41,11 @@ template <int MODE>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(
     const float* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const float* __restrict__ B, float* __restrict__ C,
-    int H, int E, int k, int Im, int mu, int n_tiles) {
+    int H, int E, int k, int Im, int mu, int n_tiles, int dense_rows) {
   __shared__ float As[FBK][FBM + 4];
   __shared__ float Bs[FBK][FBN + 4];
 
-  const fast::Tile ti = fast::decode<FBM>(offsets, E, n_tiles);
+  const fast::Tile ti = fast::decode<FBM>(offsets, E, n_tiles, dense_rows);
   if (!ti.valid) return;
 
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
   const float* a_src;
   {
     const int p = min(ti.m0 + lr, ti.seg_end - 1);
-    a_src = (MODE == kW13) ? A + (size_t)(perm[p] / k) * H : A + (size_t)p * lda;
+    const int xr = offsets == nullptr ? p : perm[p] / k;  // dense segment: x row p
+    a_src = (MODE == kW13) ? A + (size_t)xr * H : A + (size_t)p * lda;
   }
   size_t b_base;
   if (MODE == kW13) {
@@ -160,7 +161,7 @@ hipError_t launch_w13_swiglu(const Shape& s, const void* x, const int32_t* perm,
     const int n_tiles = s.mu * (s.Im / 32);
     const unsigned g = grid_size(fast::max_m_tiles(s.R(), s.E, FBM) * n_tiles);
     hipLaunchKernelGGL(grouped_gemm_f32<kW13>, dim3(g), dim3(256), 0, st, (const float*)x, perm,
-                       offsets, (const float*)w1, (float*)h, s.H, s.E, s.k, s.Im, s.mu, n_tiles);
+                       offsets, (const float*)w1, (float*)h, s.H, s.E, s.k, s.Im, s.mu, n_tiles, s.T);
   }
   return hipGetLastError();
 }
@@ -174,7 +175,7 @@ hipError_t launch_down(const Shape& s, const void* h, const int32_t* offsets, co
     const unsigned g = grid_size(fast::max_m_tiles(s.R(), s.E, FBM) * n_tiles);
     hipLaunchKernelGGL(grouped_gemm_f32<kDown>, dim3(g), dim3(256), 0, st, (const float*)h,
                        nullptr, offsets, (const float*)w2, (float*)y, s.H, s.E, s.k, s.Im, s.mu,
-                       n_tiles);
+                       n_tiles, s.T);
   }
   return hipGetLastError();
 }

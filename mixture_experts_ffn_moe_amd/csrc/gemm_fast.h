@@ -100,14 +100,18 @@ struct BoolTag {
 
 // Logical tile of this workgroup (expert-major, then n-tile, then m-tile),
 // decoded from the device-side offsets; XCD-aware: XCD x (= blockIdx % 8)
-// takes the contiguous logical range [x*per, (x+1)*per).
+// takes the contiguous logical range [x*per, (x+1)*per).  offsets == nullptr
+// is one dense segment of dense_rows rows (E = 1: the shared expert).
 template <int BM>
-__device__ __forceinline__ Tile decode(const int32_t* __restrict__ offsets, int E, int n_tiles) {
+__device__ __forceinline__ Tile decode(const int32_t* __restrict__ offsets, int E, int n_tiles,
+                                       int dense_rows) {
   __shared__ int s_info[5];
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     int off = 0, cnt = 0;
-    if (lane < E) {
+    if (offsets == nullptr) {
+      cnt = lane == 0 ? dense_rows : 0;
+    } else if (lane < E) {
       off = offsets[lane];
       cnt = offsets[lane + 1] - off;
     }
@@ -157,11 +161,15 @@ __device__ __forceinline__ Tile decode(const int32_t* __restrict__ offsets, int 
 // (ceil(cnt / mt) rounded up to 16 rows, the last one shorter); t.seg_end is
 // the end of this tile's rows.  Equal tiles take equal time, so the m-tiles
 // that share an n-tile of weights run side by side and share it in L2.
+// offsets == nullptr is one dense segment of dense_rows rows, as in decode().
 template <int BM, bool EQ = true>
-__device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets, int E, int n_tiles) {
+__device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets, int E, int n_tiles,
+                                            int dense_rows) {
   const int lane = threadIdx.x & 63;
   int off = 0, cnt = 0;
-  if (lane < E) {
+  if (offsets == nullptr) {
+    cnt = lane == 0 ? dense_rows : 0;
+  } else if (lane < E) {
     off = offsets[lane];
     cnt = offsets[lane + 1] - off;
   }
@@ -203,11 +211,11 @@ template <class C, bool PART = true, bool EQ = true>
 __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B, uint16_t* __restrict__ Cout,
-    int H, int E, int k, int Im, int mu, int n_tiles) {
+    int H, int E, int k, int Im, int mu, int n_tiles, int dense_rows) {
   // A ring (STAGES slots of BM x BK) followed by the B ring (SB slots of BN x BK)
   __shared__ __attribute__((aligned(1024))) uint16_t smem[(C::STAGES * C::BM + C::SB * C::BN) * C::BK];
 
-  const Tile ti = decode_wave<C::BM, EQ>(offsets, E, n_tiles);
+  const Tile ti = decode_wave<C::BM, EQ>(offsets, E, n_tiles, dense_rows);
   if (!ti.valid) return;
 
   const int lane = threadIdx.x & 63;
@@ -235,7 +243,10 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const int row = (wave + C::NW * i) * C::RPI + lrow;
     const int c = lpos ^ swz<C::CPR>(row);
     const int p = min(ti.m0 + row, ti.seg_end - 1);
-    const uint32_t r = (C::MODE == kW13) ? (uint32_t)(perm[p] / k) * (uint32_t)H : (uint32_t)p * (uint32_t)lda;
+    // A row: x row of route perm[p] (w13), row p of h (down); a dense
+    // segment (no offsets) reads x row p
+    const uint32_t xr = offsets == nullptr ? (uint32_t)p : (uint32_t)(perm[p] / k);
+    const uint32_t r = (C::MODE == kW13) ? xr * (uint32_t)H : (uint32_t)p * (uint32_t)lda;
     a_off[i] = (r + c * 8) * 2u;
   }
   const uint16_t* b_base;
@@ -436,6 +447,8 @@ inline long long max_m_tiles(long long R, int E, int bm) {
   return a < 1 ? 1 : a;
 }
 
+// offsets == nullptr: one dense segment of the T rows (E = k = mu = 1, the
+// shared expert), A rows read in order.
 template <class C, bool PART = true, bool EQ = true>
 hipError_t launch(const void* a, const int32_t* perm, const int32_t* offsets, const void* b,
                   void* c, int T, int H, int E, int k, int Im, int mu, hipStream_t st) {
@@ -444,7 +457,7 @@ hipError_t launch(const void* a, const int32_t* perm, const int32_t* offsets, co
   const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
   hipLaunchKernelGGL((grouped_gemm<C, PART, EQ>), dim3(grid), dim3(C::NTHR), 0, st,
                      (const uint16_t*)a, perm, offsets, (const uint16_t*)b, (uint16_t*)c, H, E, k,
-                     Im, mu, n_tiles);
+                     Im, mu, n_tiles, T);
   return hipGetLastError();
 }
 

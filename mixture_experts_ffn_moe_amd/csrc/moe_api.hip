@@ -1,9 +1,11 @@
 // C ABI of the MoE library: host-side validation, workspace layout and the
-// launch sequence.  Declarations and argument semantics: moe_mi355x.h.
+// launch sequence.  Declarations and argument semantics: moe_mi355x.h and,
+// for the shared expert, moe_shared.h.
 //
 // Every entry point validates everything it can on the host before any HIP
 // call, so a rejected call enqueues nothing and touches no output.
 #include "../../include/moe_mi355x.h"
+#include "../../include/moe_shared.h"
 #include "moe_common.h"
 
 #include <algorithm>
@@ -76,6 +78,90 @@ void layout_of(const Shape& s, moe_workspace_layout* L) {
   L->scratch = o;
   o = align_up(o + std::max(moe::decode_scratch_bytes(), moe::route_hist_bytes(s)));
   L->total = o;
+}
+
+// The shared expert's width against the envelope (moe_shared.h).
+moe_status check_shared(const Shape& s, int32_t Is) {
+  if (Is <= 0) return MOE_ERR_INVALID_ARG;
+  if (Is % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long lim = (1ll << 31) - 1;
+  if ((long long)s.T * Is > lim || 2ll * Is * s.H > lim || 4ll * Is * s.H > 0xffffffffll)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// moe_forward's workspace, then hs [T, Is] and ys [T, H].
+void shared_layout_of(const Shape& s, int Is, moe_shared_layout* L) {
+  moe_workspace_layout base;
+  layout_of(s, &base);
+  size_t o = base.total;
+  L->hs = o; o = align_up(o + (size_t)s.T * Is * elem_bytes(s));
+  L->ys = o; o = align_up(o + (size_t)s.T * s.H * elem_bytes(s));
+  L->total = o;
+}
+
+// The shared expert as the grouped GEMMs see it: one expert, one route per
+// token, one micro of width Is; its launches pass no offsets (one dense
+// segment of the T tokens in order).
+Shape dense_shape(const Shape& s, int Is) {
+  Shape d = s;
+  d.E = 1;
+  d.k = 1;
+  d.Im = Is;
+  d.mu = 1;
+  return d;
+}
+
+struct SharedArgs {
+  int Is;
+  const void* w1s;
+  const void* w2s;
+  moe_shared_layout L;
+};
+
+// moe_forward and moe_forward_shared (sh == nullptr: no shared expert).
+moe_status forward_impl(const Shape& s, const void* x, const float* wg, const float* bias,
+                        const void* w1, const void* w2, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t st, const SharedArgs* sh) {
+  moe_workspace_layout L;
+  layout_of(s, &L);
+  const size_t need = sh ? sh->L.total : L.total;
+  if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOE_ERR_UNSUPPORTED;
+
+  char* ws = (char*)workspace;
+  float* logits = (float*)(ws + L.logits);
+  int32_t* ids = (int32_t*)(ws + L.topk_ids);
+  float* w = (float*)(ws + L.topk_w);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  int32_t* inv = (int32_t*)(ws + L.inv);
+  void* h = ws + L.h;
+  void* y = ws + L.y;
+
+  if (moe::decode_supported(s) && (sh == nullptr || moe::decode_shared_supported(sh->Is))) {
+    moe::SharedExpert se;
+    if (sh) se = moe::SharedExpert{sh->w1s, sh->w2s, sh->Is, ws + sh->L.hs};
+    return hip_status(moe::launch_decode(s, x, wg, bias, w1, w2, out, logits, ids, w, counts,
+                                         offsets, perm, inv, h, ws + L.scratch, st,
+                                         sh ? &se : nullptr));
+  }
+  int32_t* hist = (int32_t*)(ws + L.scratch);
+  MOE_CHECK(hip_status(moe::launch_route(s, x, wg, bias, logits, ids, w, st, hist)));
+  MOE_CHECK(hip_status(moe::launch_permute_hist(s, ids, hist, counts, offsets, perm, inv, st)));
+  MOE_CHECK(hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, st)));
+  MOE_CHECK(hip_status(moe::launch_down(s, h, offsets, w2, y, st)));
+  void* ys = nullptr;
+  if (sh) {
+    const Shape d = dense_shape(s, sh->Is);
+    void* hs = ws + sh->L.hs;
+    ys = ws + sh->L.ys;
+    MOE_CHECK(hip_status(moe::launch_w13_swiglu(d, x, nullptr, nullptr, sh->w1s, hs, st)));
+    MOE_CHECK(hip_status(moe::launch_down(d, hs, nullptr, sh->w2s, ys, st)));
+  }
+  MOE_CHECK(hip_status(moe::launch_finalize(s, y, inv, w, out, st, ys)));
+  return MOE_OK;
 }
 
 }  // namespace
@@ -178,33 +264,73 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, c
   MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(wg)); MOE_CHECK(check_ptr(w1));
   MOE_CHECK(check_ptr(w2)); MOE_CHECK(check_ptr(out));
   if (bias != nullptr) MOE_CHECK(check_ptr(bias));
-  moe_workspace_layout L;
-  layout_of(s, &L);
-  if (workspace == nullptr || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MOE_ERR_UNSUPPORTED;
+  return forward_impl(s, x, wg, bias, w1, w2, out, workspace, workspace_bytes, (hipStream_t)stream,
+                      nullptr);
+}
 
-  char* ws = (char*)workspace;
-  float* logits = (float*)(ws + L.logits);
-  int32_t* ids = (int32_t*)(ws + L.topk_ids);
-  float* w = (float*)(ws + L.topk_w);
-  int32_t* counts = (int32_t*)(ws + L.counts);
-  int32_t* offsets = (int32_t*)(ws + L.offsets);
-  int32_t* perm = (int32_t*)(ws + L.perm);
-  int32_t* inv = (int32_t*)(ws + L.inv);
-  void* h = ws + L.h;
-  void* y = ws + L.y;
-  hipStream_t st = (hipStream_t)stream;
+// ---- shared expert (moe_shared.h)
 
-  if (moe::decode_supported(s))
-    return hip_status(moe::launch_decode(s, x, wg, bias, w1, w2, out, logits, ids, w, counts,
-                                         offsets, perm, inv, h, ws + L.scratch, st));
-  int32_t* hist = (int32_t*)(ws + L.scratch);
-  MOE_CHECK(hip_status(moe::launch_route(s, x, wg, bias, logits, ids, w, st, hist)));
-  MOE_CHECK(hip_status(moe::launch_permute_hist(s, ids, hist, counts, offsets, perm, inv, st)));
-  MOE_CHECK(hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, st)));
-  MOE_CHECK(hip_status(moe::launch_down(s, h, offsets, w2, y, st)));
-  MOE_CHECK(hip_status(moe::launch_finalize(s, y, inv, w, out, st)));
+size_t moe_shared_workspace_size(const moe_shape* shape, int32_t Is) {
+  Shape s;
+  if (check_shape(shape, &s) != MOE_OK || check_shared(s, Is) != MOE_OK) return 0;
+  moe_shared_layout L;
+  shared_layout_of(s, Is, &L);
+  return L.total;
+}
+
+moe_status moe_get_shared_workspace_layout(const moe_shape* shape, int32_t Is,
+                                           moe_shared_layout* layout) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  MOE_CHECK(check_shared(s, Is));
+  if (layout == nullptr) return MOE_ERR_INVALID_ARG;
+  shared_layout_of(s, Is, layout);
   return MOE_OK;
+}
+
+moe_status moe_shared_ffn(const moe_shape* shape, int32_t Is, const void* x, const void* w1s,
+                          const void* w2s, void* hs, void* ys, void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  MOE_CHECK(check_shared(s, Is));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(w1s)); MOE_CHECK(check_ptr(w2s));
+  MOE_CHECK(check_ptr(hs)); MOE_CHECK(check_ptr(ys));
+  hipStream_t st = (hipStream_t)stream;
+  const Shape d = dense_shape(s, Is);
+  MOE_CHECK(hip_status(moe::launch_w13_swiglu(d, x, nullptr, nullptr, w1s, hs, st)));
+  return hip_status(moe::launch_down(d, hs, nullptr, w2s, ys, st));
+}
+
+moe_status moe_finalize_shared(const moe_shape* shape, const void* y, const int32_t* inv,
+                               const float* topk_w, const void* ys, void* out, void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(y)); MOE_CHECK(check_ptr(inv)); MOE_CHECK(check_ptr(topk_w));
+  MOE_CHECK(check_ptr(ys)); MOE_CHECK(check_ptr(out));
+  return hip_status(moe::launch_finalize(s, y, inv, topk_w, out, (hipStream_t)stream, ys));
+}
+
+moe_status moe_forward_shared(const moe_shape* shape, int32_t Is, const void* x, const float* wg,
+                              const float* bias, const void* w1, const void* w2, const void* w1s,
+                              const void* w2s, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  MOE_CHECK(check_shared(s, Is));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(wg)); MOE_CHECK(check_ptr(w1));
+  MOE_CHECK(check_ptr(w2)); MOE_CHECK(check_ptr(w1s)); MOE_CHECK(check_ptr(w2s));
+  MOE_CHECK(check_ptr(out));
+  if (bias != nullptr) MOE_CHECK(check_ptr(bias));
+  SharedArgs sh;
+  sh.Is = Is;
+  sh.w1s = w1s;
+  sh.w2s = w2s;
+  shared_layout_of(s, Is, &sh.L);
+  return forward_impl(s, x, wg, bias, w1, w2, out, workspace, workspace_bytes, (hipStream_t)stream,
+                      &sh);
 }
 
 }  // extern "C"

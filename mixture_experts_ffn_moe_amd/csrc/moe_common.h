@@ -127,15 +127,26 @@ hipError_t launch_w13_swiglu(const Shape& s, const void* x, const int32_t* perm,
 hipError_t launch_down(const Shape& s, const void* h, const int32_t* offsets, const void* w2,
                        void* y, hipStream_t st);
 
+// ys: the shared expert's output [T, H] added after the routed sum, or nullptr.
 hipError_t launch_finalize(const Shape& s, const void* y, const int32_t* inv, const float* w,
-                           void* out, hipStream_t st);
+                           void* out, hipStream_t st, const void* ys = nullptr);
 
 // Small-token path (decode.hip).
 size_t decode_scratch_bytes();
 bool decode_supported(const Shape& s);
+// Shared expert of the small-token path: gate|up weights w1 [2*Is, H], down
+// weights w2 [H, Is], its SwiGLU activations written to h [T, Is].
+struct SharedExpert {
+  const void* w1;
+  const void* w2;
+  int Is;
+  void* h;
+};
+bool decode_shared_supported(int Is);
 hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const float* bias,
                          const void* w1, const void* w2, void* out, float* logits, int32_t* ids,
                          float* w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                         void* h, void* scratch, hipStream_t st);
+                         void* h, void* scratch, hipStream_t st,
+                         const SharedExpert* shared = nullptr);
 
 }  // namespace moe

@@ -4,7 +4,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import MOE_BF16, moe_forward, moe_get_workspace_layout, moe_workspace_size
+from ._lib import (MOE_BF16, moe_forward, moe_forward_shared, moe_get_shared_workspace_layout,
+                   moe_get_workspace_layout, moe_shared_workspace_size, moe_workspace_size)
 
 
 def _dtype(shape) -> torch.dtype:
@@ -38,16 +39,37 @@ def workspace_views(shape, ws: torch.Tensor) -> dict:
 
 
 class MoELayerBuffers:
-    """Output and workspace of one layer shape, allocated once with torch."""
+    """Output and workspace of one layer shape, allocated once with torch.
+    With shared_Im the workspace also holds the shared expert's regions and
+    forward_shared runs the layer with its shared expert."""
 
-    def __init__(self, shape, device="cuda"):
+    def __init__(self, shape, device="cuda", shared_Im=None):
         self.shape = shape
-        self.workspace = torch.empty(moe_workspace_size(shape), dtype=torch.uint8, device=device)
+        self.shared_Im = shared_Im
+        n = moe_workspace_size(shape) if shared_Im is None else moe_shared_workspace_size(shape, shared_Im)
+        if n == 0:
+            raise ValueError("shape (or shared_Im) outside the library's envelope")
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
         self.out = torch.empty(shape.T, shape.H, dtype=_dtype(shape), device=device)
 
     def forward(self, x, wg, bias, w1, w2, stream=None) -> torch.Tensor:
         moe_forward(self.shape, x, wg, bias, w1, w2, self.out, self.workspace, stream)
         return self.out
 
+    def forward_shared(self, x, wg, bias, w1, w2, w1s, w2s, stream=None) -> torch.Tensor:
+        if self.shared_Im is None:
+            raise ValueError("buffers were allocated without shared_Im")
+        moe_forward_shared(self.shape, self.shared_Im, x, wg, bias, w1, w2, w1s, w2s, self.out,
+                           self.workspace, stream)
+        return self.out
+
     def views(self) -> dict:
-        return workspace_views(self.shape, self.workspace)
+        v = workspace_views(self.shape, self.workspace)
+        if self.shared_Im is not None:
+            Ls = moe_get_shared_workspace_layout(self.shape, self.shared_Im)
+            dt = _dtype(self.shape)
+            es = 2 if dt == torch.bfloat16 else 4
+            T, H, Is = self.shape.T, self.shape.H, self.shared_Im
+            v["hs"] = self.workspace[Ls["hs"]:Ls["hs"] + T * Is * es].view(dt).view(T, Is)
+            v["ys"] = self.workspace[Ls["ys"]:Ls["ys"] + T * H * es].view(dt).view(T, H)
+        return v

@@ -34,6 +34,7 @@ TAG_WG = 2
 TAG_W13 = 3
 TAG_DOWN = 4
 TAG_BIAS = 5
+TAG_SHARED = 6
 
 F32 = "f32"
 BF16 = "bf16"
@@ -195,6 +196,23 @@ def make_router(sp: LayerSpec):
         z = sp.zipf_bias
         bias = zipf_bias(sp.E, z["s"], z["scale"], z["seed"])
     return wg, bias
+
+
+def shared_width(sp: LayerSpec) -> int:
+    """Intermediate width of the layer's shared expert on this rank: the
+    pages give no shape for it, so it takes one routed expert's width on the
+    rank (the whole TP shard I, not split into micros)."""
+    return sp.I
+
+
+def make_shared(sp: LayerSpec, Is: Optional[int] = None):
+    """The shared expert's weights, in the layer's dtype: w1s [2*Is, H] (gate
+    rows, then the matching up rows) and w2s [H, Is], both sigma_w * N(0, 1)
+    from the layer's stream under their own tag."""
+    Is = shared_width(sp) if Is is None else Is
+    w1s = normal_f32(sp.layer_seed, TAG_SHARED, 0, (2 * Is, sp.H), sp.sigma_w)
+    w2s = normal_f32(sp.layer_seed, TAG_SHARED, 1, (sp.H, Is), sp.sigma_w)
+    return _cast(sp, w1s), _cast(sp, w2s)
 
 
 def make_layer(sp, weights: bool = True) -> LayerInputs:

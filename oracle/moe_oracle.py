@@ -37,6 +37,11 @@ What is computed, and where the pages state it:
   finalize formula).
 * Finalize: out[t] = sum_j w[t, j] * Y[row of route (t, j)], the scale applied
   once and the top-k reduction done once (hybrid parallelism, section 6.1).
+* Shared expert: every token also passes through a shared expert whose output
+  joins the routed experts' (CANN NPU, section 3.1, where it runs on a second
+  stream).  No shape or gate is given for it; the reading taken here is an
+  expert of the same SwiGLU form applied to every token and added with
+  weight 1 after the routed sum.
 
 Precision: float64 for everything after routing (the layer's own precision
 is not fixed by the pages beyond the fp32 gate); routing weights are rounded
@@ -239,6 +244,27 @@ def forward(inp: LayerInputs, routing: Optional[dict] = None) -> dict:
         Y[a:b] = expert_ffn(Xp[a:b], w1s, w2s, sp.Im)
     out = finalize(Y, r["inv"], r["w"])
     return dict(r, Y=Y, out=out)
+
+
+def shared_expert(inp: LayerInputs, w1s: np.ndarray, w2s: np.ndarray, tokens=None) -> np.ndarray:
+    """The shared expert on every token (or on the listed tokens): the expert
+    FFN above with one micro of width Is, float64.  w1s [2Is, H] (gate rows,
+    then up rows), w2s [H, Is]."""
+    sp = inp.spec
+    x32 = widen(inp.x, sp.dtype)
+    if tokens is not None:
+        x32 = x32[np.asarray(tokens, dtype=np.int64)]
+    Is = w2s.shape[1]
+    return expert_ffn(x32, [widen(w1s, sp.dtype)], [widen(w2s, sp.dtype)], Is)
+
+
+def forward_shared(inp: LayerInputs, w1s: np.ndarray, w2s: np.ndarray,
+                   routing: Optional[dict] = None) -> dict:
+    """The layer with its shared expert: out = the routed output + the shared
+    expert's output (float64).  Also returns Ys, the shared output alone."""
+    r = forward(inp, routing)
+    ys = shared_expert(inp, w1s, w2s)
+    return dict(r, Ys=ys, out=r["out"] + ys)
 
 
 def token_outputs(inp: LayerInputs, routing: dict, tokens) -> np.ndarray:

@@ -173,3 +173,57 @@ def test_binding_checks_tensors_before_the_call(m):
         m.moe_route(s, x, wg, None, torch.zeros(4, 8), torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
     with pytest.raises(ValueError, match="workspace"):
         m.moe_forward(s, x, wg, None, x, x, x, None)
+
+
+# ---------------------------------------------------------------- shared expert (moe_shared.h)
+
+
+def test_shared_workspace_layout(m):
+    s = m.make_shape(4096, 4096, 64, 8, 1536, 1, "bf16")
+    base = m.moe_workspace_size(s)
+    Ls = m.moe_get_shared_workspace_layout(s, 1536)
+    assert Ls["total"] == m.moe_shared_workspace_size(s, 1536)
+    # the routed workspace comes first, unchanged; then hs [T, Is] and ys [T, H]
+    assert Ls["hs"] == base
+    assert Ls["ys"] - Ls["hs"] >= 4096 * 1536 * 2
+    assert Ls["total"] - Ls["ys"] >= 4096 * 4096 * 2
+    assert all(v % 256 == 0 for v in Ls.values())
+
+
+@pytest.mark.parametrize("Is,code", [
+    (0, "MOE_ERR_INVALID_ARG"), (-128, "MOE_ERR_INVALID_ARG"),
+    (96, "MOE_ERR_UNSUPPORTED"), (1 << 20, "MOE_ERR_UNSUPPORTED"),
+])
+def test_shared_width_validation(m, Is, code):
+    s = m.make_shape(64, 4096, 8, 2, 128, 1, "bf16")
+    want = getattr(m, code)
+    assert m.moe_shared_workspace_size(s, Is) == 0
+    lib = m._lib.lib
+    P = ctypes.c_void_p(4096)
+    assert lib.moe_shared_ffn(ctypes.byref(s), Is, P, P, P, P, P, None) == want
+    assert lib.moe_forward_shared(ctypes.byref(s), Is, P, P, None, P, P, P, P, P, P,
+                                  ctypes.c_size_t(1 << 40), None) == want
+
+
+def test_shared_pointer_and_workspace_validation(m):
+    lib = m._lib.lib
+    s = m.make_shape(64, 256, 8, 2, 128, 1, "bf16")
+    Is = 128
+    need = m.moe_shared_workspace_size(s, Is)
+    assert need > m.moe_workspace_size(s)
+    P = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    call = lambda w1s, w2s, ws_, n: lib.moe_forward_shared(  # noqa: E731
+        ctypes.byref(s), Is, P, P, None, P, P, w1s, w2s, P, ws_, ctypes.c_size_t(n), None)
+    assert call(None, P, ws, need) == m.MOE_ERR_INVALID_ARG
+    assert call(P, ctypes.c_void_p(4096 + 4), ws, need) == m.MOE_ERR_UNSUPPORTED
+    # the routed layer's workspace is not enough
+    assert call(P, P, ws, m.moe_workspace_size(s)) == m.MOE_ERR_WORKSPACE
+    assert call(P, P, None, need) == m.MOE_ERR_WORKSPACE
+    assert lib.moe_finalize_shared(ctypes.byref(s), P, P, P, None, P, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_shared_ffn(ctypes.byref(s), Is, P, P, P, None, P, None) == m.MOE_ERR_INVALID_ARG
+    # T == 0 enqueues nothing
+    s0 = m.make_shape(0, 256, 8, 2, 128, 1, "bf16")
+    assert lib.moe_forward_shared(ctypes.byref(s0), Is, P, P, None, P, P, P, P, P, P,
+                                  ctypes.c_size_t(0), None) == m.MOE_OK
+    assert lib.moe_shared_ffn(ctypes.byref(s0), Is, P, P, P, P, P, None) == m.MOE_OK

@@ -379,6 +379,133 @@ def test_decode_path(m, case):
     say(f"[parity] decode: out max-abs {ma:.2e} rel-L2 {rl:.2e}")
 
 
+# ------------------------------------------------------------------ shared expert
+
+SHARED = [
+    dict(name="tiny_fp32", layer="tiny_fp32"),
+    dict(name="bf16_ragged", T=1000, H=512, E=6, k=3, Im=256, micro=1, dtype=mi.BF16, seed=12),
+    dict(name="bf16_two_micro", T=300, H=256, E=8, k=2, Im=128, micro=2, dtype=mi.BF16, seed=41,
+         sigma_g=0.02, sigma_w=0.02),
+    dict(name="f32_two_micro", T=200, H=256, E=8, k=2, Im=128, micro=2, dtype=mi.F32, seed=14),
+    dict(name="bf16_one_row_tail", T=321, H=768, E=4, k=1, Im=384, micro=1, dtype=mi.BF16, seed=42,
+         sigma_g=0.02, sigma_w=0.02),
+]
+
+
+def shared_device(sp, w1s, w2s):
+    return to_dev(w1s, sp.dtype), to_dev(w2s, sp.dtype)
+
+
+@pytest.mark.parametrize("case", SHARED, ids=[c["name"] for c in SHARED])
+def test_shared_expert_layer(m, case):
+    """moe_forward_shared against the oracle (routing bit for bit, every
+    output element within the bar), the shared output ys against the
+    oracle's, and the step-wise entry points (moe_shared_ffn and
+    moe_finalize_shared after the routed steps) against the one call, bit
+    for bit (same kernels, same order)."""
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    sp = small_spec(case)
+    say(f"[parity] shared expert {case['name']}: T={sp.T} H={sp.H} E={sp.E} k={sp.k} I={sp.I}")
+    inp = mi.make_layer(sp)
+    w1s, w2s = mi.make_shared(sp)
+    Is = w2s.shape[1]
+    ref = o.forward_shared(inp, w1s, w2s)
+    d = device_inputs(inp)
+    dw1s, dw2s = shared_device(sp, w1s, w2s)
+    buf = MoELayerBuffers(shape_of(sp), shared_Im=Is)
+    out = buf.forward_shared(d["x"], d["wg"], d["bias"], d["w1"], d["w2"], dw1s, dw2s)
+    torch.cuda.synchronize()
+    v = buf.views()
+    check_routing(sp, inp, v, ref)
+    ma, rl = assert_close(to_host_f32(out), ref["out"], sp.dtype, "out with shared expert")
+    assert_close(to_host_f32(v["ys"]), ref["Ys"], sp.dtype, "shared output ys")
+    # step-wise
+    s = shape_of(sp)
+    steps = run_steps(m, sp, d)
+    hs = torch.empty(sp.T, Is, dtype=out_dtype(sp), device="cuda")
+    ys = torch.empty(sp.T, sp.H, dtype=out_dtype(sp), device="cuda")
+    out2 = torch.empty_like(out)
+    m.moe_shared_ffn(s, Is, d["x"], dw1s, dw2s, hs, ys)
+    m.moe_finalize_shared(s, steps["y"], steps["inv"], steps["w"], ys, out2)
+    torch.cuda.synchronize()
+    view = (lambda t: t.view(torch.int16)) if sp.dtype == mi.BF16 else (lambda t: t)
+    assert torch.equal(view(hs), view(v["hs"]))
+    assert torch.equal(view(ys), view(v["ys"]))
+    assert torch.equal(view(out2), view(out))
+    say(f"[parity] shared expert {case['name']}: out max-abs {ma:.2e} rel-L2 {rl:.2e}")
+
+
+SHARED_DECODE = [
+    dict(T=1, H=2048, E=8, k=2, Im=256, micro=1, seed=51),
+    dict(T=8, H=2048, E=16, k=4, Im=256, micro=2, seed=52),
+    dict(T=16, H=4096, E=64, k=8, Im=256, micro=1, seed=53),
+    # ~5300 column units: more than one unit per wave in the w13 work split
+    dict(T=16, H=2048, E=32, k=8, Im=1280, micro=2, seed=54),
+]
+
+
+@pytest.mark.parametrize("case", SHARED_DECODE,
+                         ids=[f"T{c['T']}_E{c['E']}_k{c['k']}_mu{c['micro']}" for c in SHARED_DECODE])
+def test_shared_expert_decode_path(m, case):
+    """moe_forward_shared with T <= 16 streams the shared expert's weights in
+    the decode kernels: routing and the shared activations hs are the same
+    bits as the token path's, the output meets the bar against the oracle
+    and against the token path."""
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    sp = mi.custom_spec(dtype=mi.BF16, name="decode", sigma_g=0.02, sigma_w=0.02, **case)
+    say(f"[parity] shared expert decode path T={sp.T} H={sp.H} E={sp.E} k={sp.k} I={sp.I}")
+    inp = mi.make_layer(sp)
+    w1s, w2s = mi.make_shared(sp)
+    Is = w2s.shape[1]
+    ref = o.forward_shared(inp, w1s, w2s)
+    d = device_inputs(inp)
+    dw1s, dw2s = shared_device(sp, w1s, w2s)
+    buf = MoELayerBuffers(shape_of(sp), shared_Im=Is)
+    out = buf.forward_shared(d["x"], d["wg"], d["bias"], d["w1"], d["w2"], dw1s, dw2s)
+    torch.cuda.synchronize()
+    v = buf.views()
+    check_routing(sp, inp, v, ref)
+    ma, rl = assert_close(to_host_f32(out), ref["out"], sp.dtype, "decode out with shared expert")
+    s = shape_of(sp)
+    hs = torch.empty(sp.T, Is, dtype=torch.bfloat16, device="cuda")
+    ys = torch.empty(sp.T, sp.H, dtype=torch.bfloat16, device="cuda")
+    m.moe_shared_ffn(s, Is, d["x"], dw1s, dw2s, hs, ys)
+    steps = run_steps(m, sp, d)
+    out2 = torch.empty_like(out)
+    m.moe_finalize_shared(s, steps["y"], steps["inv"], steps["w"], ys, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(hs.view(torch.int16), v["hs"].view(torch.int16))
+    e2 = errors(to_host_f32(out), to_host_f32(out2))
+    assert e2[0] <= 2 * TOL[mi.BF16][0] and e2[1] <= 2 * TOL[mi.BF16][1], e2
+    say(f"[parity] shared expert decode: out max-abs {ma:.2e} rel-L2 {rl:.2e}")
+
+
+@pytest.mark.parametrize("name", ["denoise_1micro", "decode"])
+def test_full_size_shared_expert(m, name):
+    """The full-size layers with their shared expert (width = the routed
+    shard's I): routing bit for bit, sampled output rows against the oracle
+    evaluated token by token (routed sum + shared expert)."""
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    sp = mi.spec(name)
+    inp = full_layer(name)
+    w1s, w2s = mi.make_shared(sp)
+    Is = w2s.shape[1]
+    say(f"[parity] full-size layer {sp.name} with shared expert Is={Is}")
+    ref = o.route(inp)
+    d = device_inputs(inp)
+    dw1s, dw2s = shared_device(sp, w1s, w2s)
+    buf = MoELayerBuffers(shape_of(sp), shared_Im=Is)
+    out = buf.forward_shared(d["x"], d["wg"], d["bias"], d["w1"], d["w2"], dw1s, dw2s)
+    torch.cuda.synchronize()
+    check_routing(sp, inp, buf.views(), ref)
+    toks = sample_tokens(sp.T)
+    want = o.token_outputs(inp, ref, toks) + o.shared_expert(inp, w1s, w2s, tokens=toks)
+    ma, rl = assert_close(to_host_f32(out)[toks], want, sp.dtype, f"{sp.name} + shared sampled rows")
+    say(f"[parity] {sp.name} + shared: sampled out max-abs {ma:.2e} rel-L2 {rl:.2e}")
+    del d, buf
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ graph replay
 
 GRAPH_CASES = {

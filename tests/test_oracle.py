@@ -279,6 +279,51 @@ def test_tiny_layer_matches_dense_bruteforce():
     np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-14)
 
 
+# ---------------------------------------------------------------- shared expert
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=40, H=48, E=8, k=2, Im=16, micro=1, seed=21),
+    dict(T=25, H=64, E=6, k=3, Im=8, micro=2, seed=22),
+])
+def test_shared_expert_matches_dense_bruteforce(cfg):
+    """The layer with its shared expert against the dense brute force with
+    the shared expert as one more expert whose coefficient is 1 for every
+    token (brute_dense's own FFN code, not the oracle's expert_ffn)."""
+    sp = mi.custom_spec(dtype=mi.F32, **cfg)
+    inp = mi.make_layer(sp)
+    w1s, w2s = mi.make_shared(sp)
+    r = o.forward_shared(inp, w1s, w2s)
+    w13s, downs = _unsharded(inp)
+    ids = np.concatenate([r["ids"], np.full((sp.T, 1), sp.E, dtype=np.int32)], axis=1)
+    w = np.concatenate([r["w"], np.ones((sp.T, 1), dtype=np.float32)], axis=1)
+    ref = o.brute_dense(o.widen(inp.x, sp.dtype), ids, w, w13s + [w1s], downs + [w2s])
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-14)
+    # the shared part is not negligible: dropping it fails the comparison
+    assert np.abs(r["Ys"]).max() > 1e3 * np.abs(r["out"] - ref).max()
+
+
+def test_shared_expert_gate_up_order_and_zero_down():
+    """Gate rows first: swapping the halves of w1s changes the output (SiLU is
+    not symmetric); a zero down projection leaves the routed layer exactly."""
+    sp = mi.custom_spec(T=12, H=32, E=4, k=2, Im=8, dtype=mi.F32, seed=23)
+    inp = mi.make_layer(sp)
+    w1s, w2s = mi.make_shared(sp)
+    Is = w2s.shape[1]
+    base = o.forward(inp)["out"]
+    r = o.forward_shared(inp, w1s, w2s)
+    sw = o.forward_shared(inp, np.concatenate([w1s[Is:], w1s[:Is]]), w2s)
+    assert np.abs(r["out"] - sw["out"]).max() > 1e-4
+    z = o.forward_shared(inp, w1s, np.zeros_like(w2s))
+    assert np.array_equal(z["out"], base)
+    # one token by hand: ys[t] = w2s @ (SiLU(g) * u)
+    x = inp.x[5].astype(np.float64)
+    g = w1s[:Is].astype(np.float64) @ x
+    u = w1s[Is:].astype(np.float64) @ x
+    ys = w2s.astype(np.float64) @ ((g / (1.0 + np.exp(-g))) * u)
+    np.testing.assert_allclose(r["Ys"][5], ys, rtol=1e-12, atol=1e-15)
+
+
 def test_token_outputs_match_forward():
     sp = mi.custom_spec(T=30, H=32, E=8, k=3, Im=8, micro=2, dtype=mi.BF16, seed=8)
     inp = mi.make_layer(sp)
