@@ -236,7 +236,7 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
 // hit 16 bank groups on both sides.  The k order inside each MFMA is the one
 // the grouped GEMMs use, so h is the same bits on both paths.
 constexpr int kStep = 64;        // k per LDS round trip
-constexpr int kStepsW13 = 2;     // k-steps of 64 whose loads are in flight together (w13)
+constexpr int kStepsW13 = 4;     // k-steps of 64 whose loads are in flight together (w13)
 constexpr int kStepsDown = 4;    // the same for the down projection
 constexpr int kDownWaves = 16;   // waves of the down+finalize workgroup (they split the experts)
 
