@@ -113,6 +113,9 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* wg, con
  *   If both x and permuted_x are non-NULL, also writes the gathered input
  *   permuted_x[p, :] = x[perm[p] / k, :] (dtype, [R, H]); the one-call path
  *   never materialises it (the w13 GEMM gathers rows itself).
+ * topk_ids must hold experts in [0, E) (as moe_route writes them); an id
+ * outside that range is clamped into it, so every write stays in bounds and
+ * perm is still a permutation, but the result is then unspecified.
  * Deterministic and atomic-free in its outputs. */
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* perm, int32_t* inv,
@@ -126,7 +129,10 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t*
  *   h[p, m*Im + i] = SiLU(g) * u with g = x[perm[p]/k] . w1[m][e][i],
  *   u = x[perm[p]/k] . w1[m][e][Im + i], e the expert whose offsets segment
  *   holds p; fp32 accumulation, SiLU(z) = z / (1 + e^-z), one rounding to
- *   dtype.  Output h [R, mu*Im] dtype. */
+ *   dtype.  Output h [R, mu*Im] dtype.
+ *   perm and offsets must be moe_permute's outputs for this shape (offsets
+ *   non-decreasing from 0 to R, perm a permutation of [0, R)): the kernels
+ *   index with them unchecked. */
 moe_status moe_grouped_gemm_w13_swiglu(const moe_shape* shape, const void* x, const int32_t* perm,
                                        const int32_t* offsets, const void* w1, void* h,
                                        void* stream);
@@ -135,14 +141,16 @@ moe_status moe_grouped_gemm_w13_swiglu(const moe_shape* shape, const void* x, co
  * parallelism, section 6.1: grouped GEMM2 per micro, partials added in fp32).
  *   w2 [mu, E, H, Im] dtype, micro-major.
  *   y[p, n] = sum_m sum_i h[p, m*Im + i] * w2[m][e][n][i], fp32 accumulation,
- *   one rounding to dtype.  Output y [R, H] dtype. */
+ *   one rounding to dtype.  Output y [R, H] dtype.  offsets as for the w13
+ *   GEMM (moe_permute's, used unchecked). */
 moe_status moe_grouped_gemm_down(const moe_shape* shape, const void* h, const int32_t* offsets,
                                  const void* w2, void* y, void* stream);
 
 /* Finalize: routing scale and top-k reduction once (hybrid parallelism,
  * section 6.1, the finalize formula).
  *   out[t, :] = sum_{j = 0..k-1} topk_w[t, j] * y[inv[t*k + j], :], fp32,
- *   j ascending, one rounding to dtype.  Output out [T, H] dtype. */
+ *   j ascending, one rounding to dtype.  Output out [T, H] dtype.  inv must
+ *   be moe_permute's (values in [0, R), used unchecked). */
 moe_status moe_finalize(const moe_shape* shape, const void* y, const int32_t* inv,
                         const float* topk_w, void* out, void* stream);
 

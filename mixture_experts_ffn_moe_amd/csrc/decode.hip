@@ -20,7 +20,7 @@
 //      whole 128-byte lines, re-lays them through LDS into MFMA B fragments
 //      (M = the expert's rows, padded to 16) and applies SwiGLU; h is rounded
 //      to bf16.
-//   4. decode_down_finalize: one workgroup per 16 output columns; its eight
+//   4. decode_down_finalize: one workgroup per 16 output columns; its 16
 //      waves split the active experts (enough loads in flight per CU), stream
 //      the matching w2 rows the same way, and put
 //      w[t, j] * y[route (t, j)] into a per-route LDS slot; the slots are then
@@ -261,9 +261,10 @@ struct WaveRows {
 // of the kW13Blocks workgroups takes an equal contiguous share of the list
 // (the list length is known only on the device), its waves taking the share's
 // units in turn: every CU streams the same number of bytes (to one unit),
-// whatever the number of active experts.  (With one workgroup per 4 units, a 43rd active expert or a shared
-// expert put three workgroups on some CUs, and those CUs, served the same
-// share of HBM bandwidth as the rest, finished ~25% later.)
+// whatever the number of active experts.  (With one workgroup per 4 units, a
+// 43rd active expert or a shared expert put three workgroups on some CUs, and
+// those CUs, served the same share of HBM bandwidth as the rest, finished
+// ~25% later.)
 constexpr int kW13Waves = 16;    // waves per workgroup; a wave takes every 16th unit of its share
 constexpr int kW13Blocks = 256;  // one workgroup per CU
 

@@ -1,3 +1,12 @@
+// Route permutation and expert offsets.
+//
+// "Hunyuan Image 3.0 hybrid parallelism", section 6.1: the flattened expert
+// ids are sorted by expert (permuted_to_expanded), the per-expert offsets
+// come from a bincount and a cumulative sum, and finalize reads the expert
+// outputs back through the inverse permutation.  Here the sort is a stable
+// counting sort (each expert's routes keep route order r = t*k + j), so perm
+// and inv are unique.
+//
 // The scatter of R routes to expert-sorted positions is spread over at most
 // 256 workgroups, each owning a contiguous route chunk [cs, ce).  A workgroup
 // needs the expert counts of all routes (for the offsets) and of the routes
@@ -27,10 +36,12 @@ constexpr int kMaxBlocks = 256;        // bounds the redundant counting to 256 *
 // Wave 0 of the workgroup: t = this lane's expert total, bf = its count
 // before the chunk.  Writes the write bases to base[] and, in workgroup 0,
 // counts and offsets; then scatters routes [cs, ce) stably by expert.
-__device__ __forceinline__ void scan_and_scatter(const int32_t* __restrict__ ids, int E, int cs, int ce, int t,
-                                 int bf, int* base, int32_t* __restrict__ counts,
-                                 int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                 int32_t* __restrict__ inv) {
+__device__ __forceinline__ void scan_and_scatter(const int32_t* __restrict__ ids, int E, int cs,
+                                                 int ce, int t, int bf, int* base,
+                                                 int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ perm,
+                                                 int32_t* __restrict__ inv) {
   const int lane = threadIdx.x & 63;
   if (lane >= E) t = 0;
   int incl = t;
