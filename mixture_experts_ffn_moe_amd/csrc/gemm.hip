@@ -138,12 +138,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 //  * 320-row tiles cover an expert of up to 640 routes in two m-tiles (256-row
 //    tiles need three once an expert passes 512, and each extra m-tile streams
 //    the expert's weight tile again): 2.3% faster for w13 at the near-uniform
-//    loads of the denoise layer.  For down the 256-row tile with a third weight
-//    slot is as fast (LDS: 2 x 32 KB of h rows + 3 x 32 KB of weights).
-//  * w13 keeps two weight slots: the third measured no faster and raised its
-//    fabric reads by 16% (the m-tiles that share a weight tile drift apart).
+//    loads of the denoise layer.  For down, 256 and 320 rows are within 2%.
+//  * Two weight slots for both.  A third slot raised w13's fabric reads by
+//    16% for no gain; for down it helped while the epilogue stored 32-byte
+//    pieces, and is 2% slower since the epilogue goes through LDS (down's
+//    256-row output tile then leaves in two passes of 128 rows).
 using W13Cfg = fast::Cfg<fast::kW13, 320, 256, 64, 2, 2, 4, 2>;
-using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4, 3>;
+using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4, 2>;
 
 
 inline unsigned grid_size(long long tiles) {

@@ -425,38 +425,49 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
   // (the down GEMM, whose tiles are short in K, ran 8% faster so).
   constexpr int OC = (C::MODE == kW13) ? C::HCOLS : C::BN;  // output columns of the tile
   constexpr int OS = OC * 2 + 16;  // LDS row stride in bytes: rows 4 banks apart
-  static_assert(C::BM * OS <= C::LDS_BYTES, "output tile fits the ring");
+  // the whole tile in one pass when it fits the ring, else one wave-row block
+  // (TM rows) per pass
+  constexpr int PASSES = (C::BM * OS <= C::LDS_BYTES) ? 1 : C::WM;
+  constexpr int PROWS = C::BM / PASSES;
+  static_assert(PROWS * OS <= C::LDS_BYTES, "output rows of a pass fit the ring");
+  constexpr int LPR = OC * 2 / 16, RPW = kWave / LPR;  // lanes per row, rows per store
   const int ldc = (C::MODE == kW13) ? mu * Im : H;
   const int cq = 4 * (lane >> 4);
-  __syncthreads();
-  char* so = reinterpret_cast<char*>(smem);
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int rt = wm * C::TM + 16 * i + (lane & 15);  // row in the tile
-    if (C::MODE == kW13) {
-#pragma unroll
-      for (int j = 0; j < C::FN / 2; ++j) {
-        f32x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = silu_f32(acc[i][j][r]) * acc[i][j + C::FN / 2][r];
-        *reinterpret_cast<uint2*>(so + rt * OS + (wn * (C::TN / 2) + 16 * j + cq) * 2) = pack_bf16x4(v);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        *reinterpret_cast<uint2*>(so + rt * OS + (wn * C::TN + 16 * j + cq) * 2) = pack_bf16x4(acc[i][j]);
-    }
-  }
-  __syncthreads();
-  constexpr int LPR = OC * 2 / 16, RPW = kWave / LPR;  // lanes per row, rows per store
   const int rows = ti.seg_end - ti.m0;
   const int col0 = (C::MODE == kW13) ? micro * Im + n0 : n0;
   const int cb = (lane % LPR) * 16;
-  for (int r0 = wave * RPW; r0 < rows; r0 += C::NW * RPW) {
-    const int rr = r0 + lane / LPR;
-    if (rr < rows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(so + rr * OS + cb);
-      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Cout + (size_t)(ti.m0 + rr) * ldc + col0) + cb) = v;
+  char* so = reinterpret_cast<char*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    __syncthreads();
+    if (PASSES == 1 || wm == pass) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int rt = wm * C::TM + 16 * i + (lane & 15) - pass * PROWS;  // row in this pass
+        if (C::MODE == kW13) {
+#pragma unroll
+          for (int j = 0; j < C::FN / 2; ++j) {
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = silu_f32(acc[i][j][r]) * acc[i][j + C::FN / 2][r];
+            *reinterpret_cast<uint2*>(so + rt * OS + (wn * (C::TN / 2) + 16 * j + cq) * 2) = pack_bf16x4(v);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            *reinterpret_cast<uint2*>(so + rt * OS + (wn * C::TN + 16 * j + cq) * 2) = pack_bf16x4(acc[i][j]);
+        }
+      }
+    }
+    __syncthreads();
+    const int prow_end = min(rows - pass * PROWS, PROWS);
+    for (int r0 = wave * RPW; r0 < prow_end; r0 += C::NW * RPW) {
+      const int rr = r0 + lane / LPR;
+      if (rr < prow_end) {
+        const uint4 v = *reinterpret_cast<const uint4*>(so + rr * OS + cb);
+        const size_t row = (size_t)(ti.m0 + pass * PROWS + rr);
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Cout + row * ldc + col0) + cb) = v;
+      }
     }
   }
 }
