@@ -333,8 +333,9 @@ __global__ __launch_bounds__(kW13Waves * 64) void decode_w13(const uint16_t* __r
         gv[q][1] = *reinterpret_cast<const uint4*>(g0 + r8 + kk);
         uv[q][0] = *reinterpret_cast<const uint4*>(u0 + kk);
         uv[q][1] = *reinterpret_cast<const uint4*>(u0 + r8 + kk);
-        av[q][0] = *reinterpret_cast<const uint4*>(arow + kk);
-        av[q][1] = *reinterpret_cast<const uint4*>(arow + kk + 32);
+        // rows past the expert's are zero: only real rows are loaded
+        av[q][0] = row_ok ? *reinterpret_cast<const uint4*>(arow + kk) : make_uint4(0, 0, 0, 0);
+        av[q][1] = row_ok ? *reinterpret_cast<const uint4*>(arow + kk + 32) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int q = 0; q < kStepsW13; ++q) {
@@ -347,7 +348,6 @@ __global__ __launch_bounds__(kW13Waves * 64) void decode_w13(const uint16_t* __r
         const uint4 uf0 = *reinterpret_cast<const uint4*>(ub + wr.rd0);
         const uint4 uf1 = *reinterpret_cast<const uint4*>(ub + wr.rd1);
         uint4 a0 = av[q][0], a1 = av[q][1];
-        if (!row_ok) a0 = a1 = make_uint4(0, 0, 0, 0);
         const bf16x8 A0 = __builtin_bit_cast(bf16x8, a0), A1 = __builtin_bit_cast(bf16x8, a1);
         accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, gf0), accg, 0, 0, 0);
         accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, uf0), accu, 0, 0, 0);
@@ -421,8 +421,8 @@ __global__ __launch_bounds__(kDownWaves * 64) void decode_down_finalize(
         const uint16_t* bp = b0 + (size_t)mm * mstride + (kg - mm * Imx);
         bv[q][0] = *reinterpret_cast<const uint4*>(bp);
         bv[q][1] = *reinterpret_cast<const uint4*>(bp + r8);
-        av[q][0] = *reinterpret_cast<const uint4*>(arow + kg);
-        av[q][1] = *reinterpret_cast<const uint4*>(arow + kg + 32);
+        av[q][0] = row_ok ? *reinterpret_cast<const uint4*>(arow + kg) : make_uint4(0, 0, 0, 0);
+        av[q][1] = row_ok ? *reinterpret_cast<const uint4*>(arow + kg + 32) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int q = 0; q < kStepsDown; ++q) {
@@ -431,7 +431,6 @@ __global__ __launch_bounds__(kDownWaves * 64) void decode_down_finalize(
         const uint4 f0 = *reinterpret_cast<const uint4*>(wb + wr.rd0);
         const uint4 f1 = *reinterpret_cast<const uint4*>(wb + wr.rd1);
         uint4 a0 = av[q][0], a1 = av[q][1];
-        if (!row_ok) a0 = a1 = make_uint4(0, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
                                                       __builtin_bit_cast(bf16x8, f0), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
