@@ -300,26 +300,71 @@ def read_hwmon(d) -> dict:
     return out
 
 
-def telemetry_during(torch, fn, calls):
-    """Median clock and power read from sysfs by the host while `calls`
-    back-to-back calls of `fn` run on the device (they are all enqueued first,
-    then the host samples until they finish)."""
-    d = hwmon_dir(torch)
-    if d is None:
+def amd_smi_gfx_clocks():
+    """Current engine clock of each XCD (MHz) from `amd-smi metric -c`, run as
+    a child process, or None where the tool is missing or its output differs."""
+    import re
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    if exe is None:
         return None
+    try:
+        r = subprocess.run([exe, "metric", "-c", "-g", "0", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    clocks = []
+
+    def walk(o):
+        if isinstance(o, dict):
+            for k, v in o.items():
+                if re.fullmatch(r"gfx_\d+", str(k)) and isinstance(v, dict) and isinstance(v.get("clk"), dict):
+                    val = v["clk"].get("value")
+                    if isinstance(val, (int, float)):
+                        clocks.append(float(val))
+                else:
+                    walk(v)
+        elif isinstance(o, list):
+            for v in o:
+                walk(v)
+
+    walk(data)
+    return clocks or None
+
+
+def telemetry_during(torch, fn, calls):
+    """Power read from sysfs (median of samples every 5 ms) and the engine
+    clock of each XCD read once with amd-smi, by the host while `calls`
+    back-to-back calls of `fn` run on the device (they are all enqueued
+    first; the clock sample counts only if the device was still busy when it
+    returned)."""
+    d = hwmon_dir(torch)
     torch.cuda.synchronize()
     done = torch.cuda.Event()
     for _ in range(calls):
         fn()
     done.record()
+    clocks = amd_smi_gfx_clocks()
+    clock_while_busy = not done.query()
     samples = []
     while not done.query():
-        samples.append(read_hwmon(d))
+        if d is not None:
+            samples.append(read_hwmon(d))
         time.sleep(0.005)
     torch.cuda.synchronize()
-    keys = sorted({k for smp in samples for k in smp})
-    res = {k: round(float(np.median([smp[k] for smp in samples if k in smp])), 1) for k in keys}
-    res.update({"samples": len(samples), "calls": calls, "source": f"{d} (sysfs, sampled every 5 ms)"})
+    res = {}
+    if samples:
+        keys = sorted({k for smp in samples for k in smp})
+        res = {k: round(float(np.median([smp[k] for smp in samples if k in smp])), 1) for k in keys}
+        res.update({"samples": len(samples), "source": f"{d} (sysfs, sampled every 5 ms)"})
+    if clocks is not None and clock_while_busy:
+        res["gfx_clock_MHz"] = {"per_xcd": clocks, "mean": round(float(np.mean(clocks)), 1),
+                                "source": "amd-smi metric -c, one sample during the loop"}
+    if not res:
+        return None
+    res["calls"] = calls
     return res
 
 
@@ -560,9 +605,10 @@ def main(argv=None):
     log("timing moe_forward")
     ms, wall_ms, buf = time_forward(moe, torch, d, args.steps, args.warmup)
     log(f"layer {ms:.4f} ms/step (wall {wall_ms:.4f})")
-    tele = telemetry_during(torch, lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"]), 300)
+    tele = telemetry_during(torch, lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"]), 3000)
     if tele is not None:
-        log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith(("_MHz", "_W"))))
+        log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith("_W"))
+            + (f" gfx_clock_mean_MHz={tele['gfx_clock_MHz']['mean']}" if "gfx_clock_MHz" in tele else ""))
     kern, counts = time_kernels(moe, torch, d, args.steps, args.warmup)
     shared = None
     if not args.no_extra:
