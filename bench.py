@@ -609,6 +609,15 @@ def main(argv=None):
     if tele is not None:
         log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith("_W"))
             + (f" gfx_clock_mean_MHz={tele['gfx_clock_MHz']['mean']}" if "gfx_clock_MHz" in tele else ""))
+    # per-call times of the same calls, each bracketed by its own events
+    fwd = lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])  # noqa: E731
+    pevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in pevs:
+        e0.record()
+        fwd()
+        e1.record()
+    torch.cuda.synchronize()
+    layer_calls = call_stats([e0.elapsed_time(e1) for e0, e1 in pevs])
     kern, counts = time_kernels(moe, torch, d, args.steps, args.warmup)
     shared = None
     if not args.no_extra:
@@ -634,6 +643,7 @@ def main(argv=None):
         "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, near-uniform routing)",
         "tokens_per_s": round(sp.T / (ms * 1e-3), 1),
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "per_call_ms": layer_calls,
         "config": {"workload": "denoise MoE layer, 1 micro-shard: T=4096 image tokens, hidden 4096, "
                                "64 experts top-8, TP2-shard intermediate 1536 (w13 [64,3072,4096], "
                                "down [64,4096,1536])",
