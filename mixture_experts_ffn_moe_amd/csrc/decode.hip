@@ -10,10 +10,11 @@
 //   1. decode_route_partial: fp64 router partial sums, the hidden dimension
 //      split over kSplit workgroups (one CU could not stream the router
 //      weights fast enough), exact products on v_mfma_f64_16x16x4_f64.
-//   2. decode_route_finish (one workgroup): fixed-order sum of the partials,
-//      bias, one fp32 rounding, top-k and weights (same rules as route.hip),
-//      expert counts and offsets, the stable permutation and its inverse, and
-//      the ascending list of active experts.
+//   2. routing finish, at the start of every decode_w13 workgroup (cheaper
+//      than a launch of its own): fixed-order sum of the partials, bias, one
+//      fp32 rounding, top-k and weights (same rules as route.hip), expert
+//      counts and offsets, the stable permutation and its inverse, and the
+//      ascending list of active experts; workgroup 0 writes them out.
 //   3. decode_w13: one wave per (active expert, 16 columns of the
 //      micro-major intermediate), the waves' units dealt evenly over one
 //      workgroup per CU; each wave streams 16 gate and 16 up rows of w1 in
@@ -133,16 +134,27 @@ __global__ __launch_bounds__(256) void decode_route_partial(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// 2. routing of the token tile in one workgroup of 16 waves.
-__global__ __launch_bounds__(1024) void decode_route_finish(
-    const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k,
+// 2. routing of the token tile, run by one workgroup of 16 waves (each
+// workgroup of decode_w13 runs it for itself at its start: the inputs are the
+// router partials, 128 KB in L2, and the work is a few microseconds, less
+// than a separate launch and kernel boundary).  Workgroup `out` writes the
+// routing outputs to memory; every workgroup keeps the offsets, the active
+// experts and the permutation in LDS for its own use.
+struct RouteLds {
+  float lg[kDecT][kMaxExperts];
+  int sids[kDecT * kMaxK];
+  uint64_t sel[kDecT];           // experts chosen by each token
+  int base[kMaxExperts];
+  int off[kMaxExperts + 1];      // expert offsets
+  int act[kMaxExperts + 1];      // active experts ascending; their number in act[kMaxExperts]
+  int perm[kDecT * kMaxK];       // permuted row -> route
+};
+
+__device__ __forceinline__ void route_finish(
+    const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k, bool out,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ topw,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, int32_t* __restrict__ active) {
-  __shared__ float lg[kDecT][kMaxExperts];
-  __shared__ int sids[kDecT * kMaxK];
-  __shared__ uint64_t sel[kDecT];  // experts chosen by each token
-  __shared__ int base[kMaxExperts];
+    int32_t* __restrict__ inv, int32_t* __restrict__ active, RouteLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   {  // logits: thread (r, e), partials summed in split order
@@ -151,15 +163,15 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
     for (int b = 0; b < kSplit; ++b) s += partial[((size_t)b * kDecT + r) * kMaxExperts + e];
     const double bb = (bias != nullptr && e < E) ? (double)bias[e] : 0.0;
     const float L = (float)(s + bb);
-    lg[r][e] = L;
-    if (r < T && e < E) logits[(size_t)r * E + e] = L;
+    S.lg[r][e] = L;
+    if (out && r < T && e < E) logits[(size_t)r * E + e] = L;
   }
   __syncthreads();
 
   {  // top-k and weights: wave = token, lane = expert (same rules as route.hip)
     const int t = wave;
     if (t < T) {
-      uint32_t key = lane < E ? orderable(lg[t][lane]) : 0u;
+      uint32_t key = lane < E ? orderable(S.lg[t][lane]) : 0u;
       bool taken = false;
       float mine = 0.0f, first = 0.0f;
       for (int j = 0; j < k; ++j) {
@@ -173,15 +185,15 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
           taken = true;
         }
         if (lane == 0) {
-          ids[(size_t)t * k + j] = win;
-          sids[t * k + j] = win;
+          if (out) ids[(size_t)t * k + j] = win;
+          S.sids[t * k + j] = win;
         }
       }
       const uint64_t chosen = __ballot(taken);
-      if (lane == 0) sel[t] = chosen;
+      if (lane == 0) S.sel[t] = chosen;
       const double ex = (lane < k) ? exp((double)mine - (double)first) : 0.0;
       const double s = wave_sum_f64(ex);
-      if (lane < k) topw[(size_t)t * k + lane] = (float)(ex / s);
+      if (out && lane < k) topw[(size_t)t * k + lane] = (float)(ex / s);
     }
   }
   __syncthreads();
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
   const int R = T * k;
   if (wave == 0) {
     int c = 0;
-    for (int t = 0; t < T; ++t) c += (int)((sel[t] >> lane) & 1ull);
+    for (int t = 0; t < T; ++t) c += (int)((S.sel[t] >> lane) & 1ull);
     int incl = c;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -200,29 +212,45 @@ __global__ __launch_bounds__(1024) void decode_route_finish(
       if (lane >= d) incl += v;
     }
     const int excl = incl - c;
-    base[lane] = excl;
+    S.base[lane] = excl;
     if (lane < E) {
-      counts[lane] = c;
-      offsets[lane] = excl;
+      S.off[lane] = excl;
+      if (out) {
+        counts[lane] = c;
+        offsets[lane] = excl;
+      }
     }
-    if (lane == E - 1) offsets[E] = incl;
+    if (lane == E - 1) {
+      S.off[E] = incl;
+      if (out) offsets[E] = incl;
+    }
     // active experts in ascending order: position = number of active experts below
     const uint64_t act = __ballot(lane < E && c > 0);
     const uint64_t below = (lane == 0) ? 0ull : (act & ((~0ull) >> (64 - lane)));
-    if (lane < E && c > 0) active[__popcll(below)] = lane;
-    if (lane == 0) active[kMaxExperts] = __popcll(act);
+    if (lane < E && c > 0) {
+      S.act[__popcll(below)] = lane;
+      if (out) active[__popcll(below)] = lane;
+    }
+    if (lane == 0) {
+      S.act[kMaxExperts] = __popcll(act);
+      if (out) active[kMaxExperts] = __popcll(act);
+    }
   }
   __syncthreads();
   // stable scatter: the routes of expert e before r = t*k + j are those of
   // the earlier tokens that chose e
   for (int r = tid; r < R; r += blockDim.x) {
-    const int t = r / k, e = sids[r];
+    const int t = r / k, e = S.sids[r];
     int rank = 0;
-    for (int q = 0; q < t; ++q) rank += (int)((sel[q] >> e) & 1ull);
-    const int p = base[e] + rank;
-    perm[p] = r;
-    inv[r] = p;
+    for (int q = 0; q < t; ++q) rank += (int)((S.sel[q] >> e) & 1ull);
+    const int p = S.base[e] + rank;
+    S.perm[p] = r;
+    if (out) {
+      perm[p] = r;
+      inv[r] = p;
+    }
   }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -268,16 +296,21 @@ struct WaveRows {
 constexpr int kW13Waves = 16;    // waves per workgroup; a wave takes every 16th unit of its share
 constexpr int kW13Blocks = 256;  // one workgroup per CU
 
-__global__ __launch_bounds__(kW13Waves * 64) void decode_w13(const uint16_t* __restrict__ x,
-                                                           const int32_t* __restrict__ perm,
-                                                           const int32_t* __restrict__ offsets,
-                                                           const int32_t* __restrict__ active,
-                                                           const uint16_t* __restrict__ w1, int T,
-                                                           int H, int E, int k, int Im, int mu,
-                                                           uint16_t* __restrict__ h,
-                                                           const uint16_t* __restrict__ w1s, int Is,
-                                                           uint16_t* __restrict__ hs) {
+__global__ __launch_bounds__(kW13Waves * 64) void decode_w13(
+    const uint16_t* __restrict__ x, const double* __restrict__ partial, const float* __restrict__ bias,
+    const uint16_t* __restrict__ w1, int T, int H, int E, int k, int Im, int mu,
+    uint16_t* __restrict__ h, const uint16_t* __restrict__ w1s, int Is, uint16_t* __restrict__ hs,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ topw,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets_out, int32_t* __restrict__ perm_out,
+    int32_t* __restrict__ inv, int32_t* __restrict__ active_out) {
+  static_assert(kW13Waves * 64 == kDecT * kMaxExperts, "routing: one thread per (token, expert)");
   __shared__ __attribute__((aligned(16))) char buf[kW13Waves][2][2048];  // per wave: gate, up
+  __shared__ RouteLds rs;
+  route_finish(partial, bias, T, E, k, blockIdx.x == 0, logits, ids, topw, counts, offsets_out, perm_out,
+               inv, active_out, rs);
+  const int* active = rs.act;
+  const int* offsets = rs.off;
+  const int* perm = rs.perm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fr = lane & 15, fk = (lane >> 4) * 8;
@@ -486,15 +519,13 @@ hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const f
   int32_t* active = (int32_t*)((char*)scratch + (size_t)kSplit * kDecT * kMaxExperts * sizeof(double));
   hipLaunchKernelGGL(decode_route_partial, dim3(kSplit), dim3(256), 0, st, (const uint16_t*)x, wg,
                      s.T, s.H, s.E, partial);
-  hipLaunchKernelGGL(decode_route_finish, dim3(1), dim3(1024), 0, st, partial, bias, s.T, s.E,
-                     s.k, logits, ids, w, counts, offsets, perm, inv, active);
   const uint16_t* w1s = shared ? (const uint16_t*)shared->w1 : nullptr;
   const uint16_t* w2s = shared ? (const uint16_t*)shared->w2 : nullptr;
   uint16_t* hs = shared ? (uint16_t*)shared->h : nullptr;
   const int Is = shared ? shared->Is : 0;
   hipLaunchKernelGGL(decode_w13, dim3(kW13Blocks), dim3(kW13Waves * 64), 0, st, (const uint16_t*)x,
-                     perm, offsets, active, (const uint16_t*)w1, s.T, s.H, s.E, s.k, s.Im, s.mu,
-                     (uint16_t*)h, w1s, Is, hs);
+                     partial, bias, (const uint16_t*)w1, s.T, s.H, s.E, s.k, s.Im, s.mu, (uint16_t*)h,
+                     w1s, Is, hs, logits, ids, w, counts, offsets, perm, inv, active);
   hipLaunchKernelGGL(decode_down_finalize, dim3(s.H / 16), dim3(kDownWaves * 64), 0, st, (const uint16_t*)h,
                      perm, offsets, active, w, (const uint16_t*)w2, s.T, s.H, s.E, s.k, s.Im,
                      s.mu, (uint16_t*)out, (const uint16_t*)hs, w2s, Is);
