@@ -300,19 +300,11 @@ def read_hwmon(d) -> dict:
     return out
 
 
-def amd_smi_gfx_clocks():
-    """Current engine clock of each XCD (MHz) from `amd-smi metric -c`, run as
-    a child process, or None where the tool is missing or its output differs."""
+def _gfx_clocks_from_json(text):
+    """Engine clock of each XCD (MHz) in `amd-smi metric -c --json` output."""
     import re
-    import shutil
-    import subprocess
-    exe = shutil.which("amd-smi")
-    if exe is None:
-        return None
     try:
-        r = subprocess.run([exe, "metric", "-c", "-g", "0", "--json"], capture_output=True, text=True,
-                           timeout=30)
-        data = json.loads(r.stdout)
+        data = json.loads(text)
     except Exception:
         return None
     clocks = []
@@ -334,34 +326,59 @@ def amd_smi_gfx_clocks():
     return clocks or None
 
 
-def telemetry_during(torch, fn, calls):
+def telemetry_during(torch, fn, chunk=200, settle_s=2.0, max_s=30.0):
     """Power read from sysfs (median of samples every 5 ms) and the engine
-    clock of each XCD read once with amd-smi, by the host while `calls`
-    back-to-back calls of `fn` run on the device (they are all enqueued
-    first; the clock sample counts only if the device was still busy when it
-    returned)."""
+    clock of each XCD read once with amd-smi (a child process), while the
+    device runs back-to-back calls of `fn`.  The calls are enqueued `chunk`
+    at a time and each chunk is waited for, so the queue stays short.  The
+    power management needs about a second of sustained load to settle, so
+    amd-smi starts after `settle_s` seconds of calls (power is sampled from
+    then on too) and the calls go on until it has returned (at most `max_s`
+    seconds in all)."""
+    import shutil
+    import subprocess
     d = hwmon_dir(torch)
+    exe = shutil.which("amd-smi")
     torch.cuda.synchronize()
-    done = torch.cuda.Event()
-    for _ in range(calls):
-        fn()
-    done.record()
-    clocks = amd_smi_gfx_clocks()
-    clock_while_busy = not done.query()
-    samples = []
-    while not done.query():
-        if d is not None:
-            samples.append(read_hwmon(d))
-        time.sleep(0.005)
+    proc, started = None, False
+    samples, calls, t0 = [], 0, time.perf_counter()
+    while True:
+        elapsed = time.perf_counter() - t0
+        if not started and elapsed >= settle_s:
+            started = True
+            if exe is not None:
+                try:
+                    proc = subprocess.Popen([exe, "metric", "-c", "-g", "0", "--json"], stdout=subprocess.PIPE,
+                                            stderr=subprocess.DEVNULL, text=True)
+                except OSError:
+                    proc = None
+        for _ in range(chunk):
+            fn()
+        calls += chunk
+        ev = torch.cuda.Event()
+        ev.record()
+        while not ev.query():
+            if d is not None and started:
+                samples.append(read_hwmon(d))
+            time.sleep(0.005)
+        elapsed = time.perf_counter() - t0
+        if (started and (proc is None or proc.poll() is not None)) or elapsed >= max_s:
+            break
+    clocks = None
+    if proc is not None:
+        if proc.poll() is None:
+            proc.kill()
+        out, _ = proc.communicate()
+        clocks = _gfx_clocks_from_json(out) if proc.returncode == 0 else None
     torch.cuda.synchronize()
     res = {}
     if samples:
         keys = sorted({k for smp in samples for k in smp})
         res = {k: round(float(np.median([smp[k] for smp in samples if k in smp])), 1) for k in keys}
         res.update({"samples": len(samples), "source": f"{d} (sysfs, sampled every 5 ms)"})
-    if clocks is not None and clock_while_busy:
+    if clocks is not None:
         res["gfx_clock_MHz"] = {"per_xcd": clocks, "mean": round(float(np.mean(clocks)), 1),
-                                "source": "amd-smi metric -c, one sample during the loop"}
+                                "source": "amd-smi metric -c, one sample while the calls ran"}
     if not res:
         return None
     res["calls"] = calls
@@ -605,10 +622,6 @@ def main(argv=None):
     log("timing moe_forward")
     ms, wall_ms, buf = time_forward(moe, torch, d, args.steps, args.warmup)
     log(f"layer {ms:.4f} ms/step (wall {wall_ms:.4f})")
-    tele = telemetry_during(torch, lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"]), 3000)
-    if tele is not None:
-        log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith("_W"))
-            + (f" gfx_clock_mean_MHz={tele['gfx_clock_MHz']['mean']}" if "gfx_clock_MHz" in tele else ""))
     # per-call times of the same calls, each bracketed by its own events
     fwd = lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])  # noqa: E731
     pevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -627,6 +640,12 @@ def main(argv=None):
                   "tokens_per_s": round(sp.T / (ms_sh * 1e-3), 1), "added_ms": round(ms_sh - ms, 4),
                   "shared_tflops": round(shared_flops(sp, Is) / ((ms_sh - ms) * 1e-3) / 1e12, 2)}
         log(f"with shared expert {ms_sh:.4f} ms")
+    # last, as it loads the device for seconds (the timings above run on a
+    # device that has not been held at its power cap for long)
+    tele = telemetry_during(torch, lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"]))
+    if tele is not None:
+        log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith("_W"))
+            + (f" gfx_clock_mean_MHz={tele['gfx_clock_MHz']['mean']}" if "gfx_clock_MHz" in tele else ""))
     log("kernels " + " ".join(f"{k}={v * 1e3:.1f}us" for k, v in kern.items()))
 
     flops = expert_flops(sp)
