@@ -578,7 +578,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-extra", action="store_true", help="skip the decode, 2-micro and skewed layers")
+    ap.add_argument("--no-extra", action="store_true", help="skip the decode, 2-micro, skewed and shared-expert layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -642,7 +642,7 @@ def main(argv=None):
         log(f"with shared expert {ms_sh:.4f} ms")
     # last, as it loads the device for seconds (the timings above run on a
     # device that has not been held at its power cap for long)
-    tele = telemetry_during(torch, lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"]))
+    tele = telemetry_during(torch, fwd)
     if tele is not None:
         log("telemetry " + " ".join(f"{k}={v}" for k, v in tele.items() if k.endswith("_W"))
             + (f" gfx_clock_mean_MHz={tele['gfx_clock_MHz']['mean']}" if "gfx_clock_MHz" in tele else ""))
