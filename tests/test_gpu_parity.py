@@ -515,8 +515,9 @@ GRAPH_CASES = {
 }
 
 
+@pytest.mark.parametrize("shared", [False, True], ids=["routed", "with_shared_expert"])
 @pytest.mark.parametrize("name", list(GRAPH_CASES))
-def test_graph_replay_matches_eager(m, name):
+def test_graph_replay_matches_eager(m, name, shared):
     """moe_forward captured once as a HIP graph and replayed six times, new
     tokens copied into the captured input between replays and an eager layer
     call on other buffers in between: every replay gives the eager call's
@@ -524,29 +525,40 @@ def test_graph_replay_matches_eager(m, name):
     only, no memsets or host work, so a capture holds the whole call)."""
     from mixture_experts_ffn_moe_amd import MoELayerBuffers
     sp = GRAPH_CASES[name]()
-    say(f"[parity] graph replay {name}: T={sp.T} H={sp.H} E={sp.E} k={sp.k}")
+    say(f"[parity] graph replay {name} shared={shared}: T={sp.T} H={sp.H} E={sp.E} k={sp.k}")
     d = device_inputs(mi.make_layer(sp))
+    Is = None
+    if shared:
+        w1s, w2s = mi.make_shared(sp)
+        Is = w2s.shape[1]
+        dw1s, dw2s = to_dev(w1s, sp.dtype), to_dev(w2s, sp.dtype)
+
+    def call(b, x):
+        if shared:
+            return b.forward_shared(x, d["wg"], d["bias"], d["w1"], d["w2"], dw1s, dw2s)
+        return b.forward(x, d["wg"], d["bias"], d["w1"], d["w2"])
+
     xs = [d["x"], torch.flip(d["x"], dims=[0]).contiguous()]
-    eager = MoELayerBuffers(shape_of(sp))
-    ref = [eager.forward(x, d["wg"], d["bias"], d["w1"], d["w2"]).clone() for x in xs]
+    eager = MoELayerBuffers(shape_of(sp), shared_Im=Is)
+    ref = [call(eager, x).clone() for x in xs]
     torch.cuda.synchronize()
     assert not torch.equal(ref[0], ref[1])
     x_static = xs[0].clone()
-    buf = MoELayerBuffers(shape_of(sp))
+    buf = MoELayerBuffers(shape_of(sp), shared_Im=Is)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        buf.forward(x_static, d["wg"], d["bias"], d["w1"], d["w2"])
+        call(buf, x_static)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        buf.forward(x_static, d["wg"], d["bias"], d["w1"], d["w2"])
+        call(buf, x_static)
     torch.cuda.synchronize()
     for i in range(6):
         x_static.copy_(xs[i % 2])
         g.replay()
-        eager.forward(xs[(i + 1) % 2], d["wg"], d["bias"], d["w1"], d["w2"])
+        call(eager, xs[(i + 1) % 2])
         torch.cuda.synchronize()
         assert torch.equal(buf.out.view(torch.int16), ref[i % 2].view(torch.int16)), f"replay {i}"
     del g
