@@ -9,7 +9,10 @@
 //
 //   1. decode_route_partial: fp64 router partial sums, the hidden dimension
 //      split over kSplit workgroups (one CU could not stream the router
-//      weights fast enough), exact products on v_mfma_f64_16x16x4_f64.
+//      weights fast enough), exact products on v_mfma_f64_16x16x4_f64; each
+//      of a workgroup's 16 waves takes a hidden quarter and 16 experts, so
+//      four waves share a SIMD's matrix pipe (one wave alone keeps it half
+//      busy).
 //   2. routing finish, at the start of every decode_w13 workgroup (cheaper
 //      than a launch of its own): fixed-order sum of the partials, bias, one
 //      fp32 rounding, top-k and weights (same rules as route.hip), expert
@@ -62,48 +65,36 @@ __device__ __forceinline__ void load8f(const uint16_t* p, float (&v)[8]) {
 
 // ---------------------------------------------------------------------------
 // 1. router partials: block s covers hidden [s*H/kSplit, (s+1)*H/kSplit), its
-// wave w a quarter of that; partial[s][t][e] (fp64, summed over the waves in
-// a fixed order).
-__global__ __launch_bounds__(256) void decode_route_partial(const uint16_t* __restrict__ x,
+// wave w the quarter w % 4 of that for experts [16*(w/4), 16*(w/4) + 16);
+// partial[s][t][e] (fp64, the quarters summed in a fixed order).
+constexpr int kRouteWaves = 16;
+__global__ __launch_bounds__(kRouteWaves * 64) void decode_route_partial(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ wg, int T,
                                                             int H, int E,
                                                             double* __restrict__ partial) {
   __shared__ double part[4][kDecT][kMaxExperts + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tl = lane & 15, g = lane >> 4;
+  const int hw = wave & 3, q = wave >> 2;  // hidden quarter, expert tile
   const int hs = H / kSplit, hq = hs / 4;
-  const int hb = blockIdx.x * hs + wave * hq;
+  const int hb = blockIdx.x * hs + hw * hq;
   // tokens past T and experts past E read the last valid row: their partials
   // are never used, so no operand is masked
   const uint16_t* xrow = x + (size_t)min(tl, T - 1) * H + hb + 8 * g;
-  const float* wrow[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = 16 * q + tl;
-    wrow[q] = wg + (size_t)min(e, E - 1) * H + hb + 8 * g;
-  }
-  f64x4 acc[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
-  float xv[2][8], wv[2][4][8];
+  const float* wrow = wg + (size_t)min(16 * q + tl, E - 1) * H + hb + 8 * g;
+  f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+  float xv[2][8], wv[2][8];
   auto load_chunk = [&](int c, int b) {
     load8f(xrow + c, xv[b]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a = *reinterpret_cast<const float4*>(wrow[q] + c);
-      const float4 bb = *reinterpret_cast<const float4*>(wrow[q] + c + 4);
-      wv[b][q][0] = a.x; wv[b][q][1] = a.y; wv[b][q][2] = a.z; wv[b][q][3] = a.w;
-      wv[b][q][4] = bb.x; wv[b][q][5] = bb.y; wv[b][q][6] = bb.z; wv[b][q][7] = bb.w;
-    }
+    const float4 a = *reinterpret_cast<const float4*>(wrow + c);
+    const float4 bb = *reinterpret_cast<const float4*>(wrow + c + 4);
+    wv[b][0] = a.x; wv[b][1] = a.y; wv[b][2] = a.z; wv[b][3] = a.w;
+    wv[b][4] = bb.x; wv[b][5] = bb.y; wv[b][6] = bb.z; wv[b][7] = bb.w;
   };
   auto mma_chunk = [&](int b) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const double a = (double)xv[b][m];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)wv[b][q][m], acc[q], 0, 0, 0);
-    }
+    for (int m = 0; m < 8; ++m)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[b][m], (double)wv[b][m], acc, 0, 0, 0);
   };
   // hq = H / 64 is a multiple of 32: pairs of chunks (the second in flight
   // while the first is consumed), then one trailing chunk when hq % 64 == 32
@@ -120,14 +111,10 @@ __global__ __launch_bounds__(256) void decode_route_partial(const uint16_t* __re
   }
   // fp64 16x16 D layout: register r holds row (lane/16) + 4r, column lane%16
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) part[wave][g + 4 * r][16 * q + tl] = acc[q][r];
+  for (int r = 0; r < 4; ++r) part[hw][g + 4 * r][16 * q + tl] = acc[r];
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;
-    const int r = idx >> 6, e = idx & 63;
+  {
+    const int r = tid >> 6, e = tid & 63;
     partial[((size_t)blockIdx.x * kDecT + r) * kMaxExperts + e] =
         ((part[0][r][e] + part[1][r][e]) + part[2][r][e]) + part[3][r][e];
   }
@@ -517,7 +504,7 @@ hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const f
                          void* h, void* scratch, hipStream_t st, const SharedExpert* shared) {
   double* partial = (double*)scratch;
   int32_t* active = (int32_t*)((char*)scratch + (size_t)kSplit * kDecT * kMaxExperts * sizeof(double));
-  hipLaunchKernelGGL(decode_route_partial, dim3(kSplit), dim3(256), 0, st, (const uint16_t*)x, wg,
+  hipLaunchKernelGGL(decode_route_partial, dim3(kSplit), dim3(kRouteWaves * 64), 0, st, (const uint16_t*)x, wg,
                      s.T, s.H, s.E, partial);
   const uint16_t* w1s = shared ? (const uint16_t*)shared->w1 : nullptr;
   const uint16_t* w2s = shared ? (const uint16_t*)shared->w2 : nullptr;
