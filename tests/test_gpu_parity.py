@@ -208,6 +208,90 @@ def test_routing_ties_toward_lower_expert(m):
     assert ids.cpu().numpy()[3].tolist() == [3, 6, 7]
 
 
+def test_empty_batch_enqueues_nothing(m):
+    """T = 0 through every entry point with real device buffers: each call
+    returns without error and leaves a sentinel-filled workspace as it was."""
+    sp = mi.custom_spec(T=0, H=256, E=8, k=2, Im=128, micro=2, dtype=mi.BF16, seed=1)
+    s = shape_of(sp)
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    buf = MoELayerBuffers(s, shared_Im=128)
+    buf.workspace.fill_(0xA5)
+    before = buf.workspace.clone()
+    bf = torch.bfloat16
+    x = torch.empty(0, sp.H, dtype=bf, device="cuda")
+    wg = torch.randn(sp.E, sp.H, device="cuda")
+    w1 = torch.zeros(sp.micro, sp.E, 2 * sp.Im, sp.H, dtype=bf, device="cuda")
+    w2 = torch.zeros(sp.micro, sp.E, sp.H, sp.Im, dtype=bf, device="cuda")
+    w1s = torch.zeros(256, sp.H, dtype=bf, device="cuda")
+    w2s = torch.zeros(sp.H, 128, dtype=bf, device="cuda")
+    assert buf.forward(x, wg, None, w1, w2).shape == (0, sp.H)
+    assert buf.forward_shared(x, wg, None, w1, w2, w1s, w2s).shape == (0, sp.H)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    L, ids, w = torch.empty(0, sp.E, device="cuda"), torch.empty(0, sp.k, **i32), torch.empty(0, sp.k, device="cuda")
+    counts, offsets = torch.full((sp.E,), -7, **i32), torch.full((sp.E + 1,), -7, **i32)
+    perm, inv = torch.empty(0, **i32), torch.empty(0, **i32)
+    h = torch.empty(0, sp.micro * sp.Im, dtype=bf, device="cuda")
+    y = torch.empty(0, sp.H, dtype=bf, device="cuda")
+    out = torch.empty(0, sp.H, dtype=bf, device="cuda")
+    m.moe_route(s, x, wg, None, L, ids, w)
+    m.moe_permute(s, ids, counts, offsets, perm, inv)
+    m.moe_grouped_gemm_w13_swiglu(s, x, perm, offsets, w1, h)
+    m.moe_grouped_gemm_down(s, h, offsets, w2, y)
+    m.moe_finalize(s, y, inv, w, out)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.workspace, before)
+    assert (counts == -7).all() and (offsets == -7).all()
+
+
+EXTREME = [
+    dict(name="token_path_bf16", T=40, H=256, E=8, k=3, Im=128, dtype=mi.BF16),
+    dict(name="token_path_f32", T=40, H=256, E=8, k=3, Im=128, dtype=mi.F32),
+    dict(name="decode_path_bf16", T=8, H=2048, E=8, k=3, Im=256, dtype=mi.BF16),
+]
+
+
+@pytest.mark.parametrize("case", EXTREME, ids=[c["name"] for c in EXTREME])
+def test_router_extreme_magnitudes(m, case):
+    """Router operands across the whole fp32 range: subnormal and tiny
+    activations, a 1e30 activation, subnormal router rows (down to the
+    smallest subnormal), a row scaled by 1e6 and an all-zero token.  Every
+    product is exact in fp64 whatever its magnitude, so the logits must still
+    match the oracle bit for bit (including the fp32-subnormal logits of the
+    subnormal rows and the +0.0 logits of the zero token) on both router
+    kernels."""
+    import dataclasses
+    c = dict(case)
+    name = c.pop("name")
+    sp = mi.custom_spec(seed=77, name=name, sigma_g=0.02, sigma_w=0.02, **c)
+    say(f"[parity] router extremes {name}: T={sp.T} H={sp.H} E={sp.E} k={sp.k}")
+    inp = mi.make_layer(sp)
+    x = o.widen(inp.x, sp.dtype).copy()
+    x[0, :16] = np.float32(1e-39) * np.sign(x[0, :16])
+    x[1, 3] = np.float32(1e30)
+    x[2] = 0.0
+    wg = inp.wg.copy()
+    wg[1] *= np.float32(1e-40)
+    wg[2, ::3] = np.float32(1.4e-45)
+    wg[3] *= np.float32(1e6)
+    xb = mi.f32_to_bf16_bits(x) if sp.dtype == mi.BF16 else x
+    inp = dataclasses.replace(inp, x=xb, wg=wg)
+    ref = o.route(inp)
+    # the subnormal row gives fp32-subnormal logits (except for the 1e30 token)
+    assert (np.abs(np.delete(ref["logits"][:, 1], 1)) < np.float32(1.2e-38)).all()
+    d = device_inputs(inp)
+    s = shape_of(sp)
+    if sp.T <= 16:
+        from mixture_experts_ffn_moe_amd import MoELayerBuffers
+        buf = MoELayerBuffers(s)
+        buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+        torch.cuda.synchronize()
+        got = buf.views()
+    else:
+        got = run_steps(m, sp, d)
+    check_routing(sp, inp, got, ref)
+    assert got["logits"][2].view(torch.int32).eq(0).all()
+
+
 # ------------------------------------------------------------------ full-size layers
 
 _CACHE = {}
