@@ -144,10 +144,12 @@ __device__ __forceinline__ void route_finish(
     int32_t* __restrict__ inv, int32_t* __restrict__ active, RouteLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  {  // logits: thread (r, e), partials summed in split order
+  {  // logits: thread (r, e), partials summed in split order (rows past T
+     // are never ranked: their partials are not read)
     const int r = tid >> 6, e = tid & 63;
     double s = 0.0;
-    for (int b = 0; b < kSplit; ++b) s += partial[((size_t)b * kDecT + r) * kMaxExperts + e];
+    if (r < T)
+      for (int b = 0; b < kSplit; ++b) s += partial[((size_t)b * kDecT + r) * kMaxExperts + e];
     const double bb = (bias != nullptr && e < E) ? (double)bias[e] : 0.0;
     const float L = (float)(s + bb);
     S.lg[r][e] = L;
