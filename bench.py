@@ -334,11 +334,15 @@ def telemetry_during(torch, fn, chunk=200, settle_s=2.0, max_s=30.0):
     power management needs about a second of sustained load to settle, so
     amd-smi starts after `settle_s` seconds of calls (power is sampled from
     then on too) and the calls go on until it has returned (at most `max_s`
-    seconds in all)."""
+    seconds in all).  Under rocprofv3 (its ROCPROF_* variables are set) no
+    child process is started: the profiler's preloaded library initialises
+    the GPU in every child, and amd-smi starts through `env`, which would
+    then replace a GPU-initialised process with another."""
     import shutil
     import subprocess
     d = hwmon_dir(torch)
-    exe = shutil.which("amd-smi")
+    under_profiler = any(key.startswith("ROCPROF") for key in os.environ)
+    exe = None if under_profiler else shutil.which("amd-smi")
     torch.cuda.synchronize()
     proc, started = None, False
     samples, calls, t0 = [], 0, time.perf_counter()
