@@ -10,6 +10,12 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # a planted oracle mistake, set only by test_oracle_mutants.py in a child process
+    mutant = os.environ.get("MOE_ORACLE_MUTANT")
+    if mutant:
+        sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+        import oracle_mutants
+        oracle_mutants.apply(mutant)
 
 
 def gpu_available() -> bool:
