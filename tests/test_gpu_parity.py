@@ -383,6 +383,63 @@ def test_full_size_stepwise_permute_matches_forward(m, name):
     torch.cuda.empty_cache()
 
 
+def test_maximum_token_count(m):
+    """The largest T the envelope takes at the denoise layer's shape: T = 65535,
+    so R * H = 524280 * 4096 sits just below 2^31 (y is 4.3 GB).  At this size
+    the routing is checked through what holds at any size: the ids are the
+    oracle's top-k of the GPU's own logits for every token, the weights its
+    renormalised softmax, counts, offsets, perm and inv the oracle's functions
+    of those ids (one-call and step-wise permutation alike); the logits match
+    the oracle bit for bit on sampled tokens, and so does the output within
+    the bar, token by token, among them the token whose route is the last
+    permuted row (the largest A-row and y-row offsets).  The tokens are the
+    denoise layer's 4096, repeated 16 times with copy i rotated by i places
+    along the hidden dimension (distinct tokens of the same distribution,
+    without drawing 268M new values)."""
+    import dataclasses
+    base = full_layer("denoise_1micro")
+    sp = dataclasses.replace(base.spec, T=65535, name="denoise_max_tokens")
+    assert sp.T * sp.k * sp.H < 2 ** 31 <= (sp.T + 1) * sp.k * sp.H * 2
+    say(f"[parity] maximum token count: T={sp.T} R={sp.T * sp.k} H={sp.H}")
+    x = np.concatenate([np.roll(base.x, i, axis=1) for i in range(16)])[:sp.T]
+    inp = mi.LayerInputs(sp, np.ascontiguousarray(x), base.wg, base.bias, base.w1, base.w2)
+    d = device_inputs(inp)
+    from mixture_experts_ffn_moe_amd import MoELayerBuffers
+    s = shape_of(sp)
+    buf = MoELayerBuffers(s)
+    out = buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    v = buf.views()
+    L = v["logits"].cpu().numpy()
+    ids = v["ids"].cpu().numpy()
+    assert np.array_equal(ids, o.select_topk(L, sp.k))
+    np.testing.assert_allclose(v["w"].cpu().numpy(), o.topk_weights(L, ids), rtol=2e-6, atol=1e-7)
+    counts = o.expert_counts(ids, sp.E)
+    perm, inv = o.route_permutation(ids)
+    assert np.array_equal(v["counts"].cpu().numpy(), counts)
+    assert np.array_equal(v["offsets"].cpu().numpy(), o.expert_offsets(counts))
+    assert np.array_equal(v["perm"].cpu().numpy(), perm) and np.array_equal(v["inv"].cpu().numpy(), inv)
+    c2, o2 = torch.empty_like(v["counts"]), torch.empty_like(v["offsets"])
+    p2, i2 = torch.empty_like(v["perm"]), torch.empty_like(v["inv"])
+    m.moe_permute(s, v["ids"], c2, o2, p2, i2)
+    torch.cuda.synchronize()
+    assert torch.equal(p2, v["perm"]) and torch.equal(i2, v["inv"]) and torch.equal(o2, v["offsets"])
+    say(f"[parity] maximum token count: routing consistent, loads {counts.min()}..{counts.max()}")
+    last = int(perm[-1]) // sp.k  # token of the last permuted row
+    toks = sorted(set(sample_tokens(sp.T, n=12, seed=5)) | {last})
+    x32 = o.widen(inp.x[toks], sp.dtype)
+    Lref = o.router_logits(x32, inp.wg, inp.bias)
+    flags = o.logits_near_midpoint(x32, inp.wg, inp.bias)
+    assert ((L[toks].view(np.uint32) == Lref.view(np.uint32)) | flags).all()
+    routing = dict(ids=ids, w=v["w"].cpu().numpy())
+    want = o.token_outputs(inp, routing, toks)
+    got = out[toks].float().cpu().numpy()
+    ma, rl = assert_close(got, want, sp.dtype, "maximum token count, sampled rows")
+    say(f"[parity] maximum token count: sampled out max-abs {ma:.2e} rel-L2 {rl:.2e}")
+    del d, buf, out, v
+    torch.cuda.empty_cache()
+
+
 def test_two_micro_equals_one_micro_full_size(m):
     """The 2-micro layer (micro-major pack) must equal the expert-major layer
     within tolerance over every output element."""
