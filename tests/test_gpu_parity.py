@@ -102,6 +102,9 @@ SMALL = [
          sigma_g=0.02, sigma_w=0.02),
     dict(name="im384_three_col_tiles", T=257, H=768, E=10, k=3, Im=384, micro=1, dtype=mi.BF16,
          seed=19, sigma_g=0.02, sigma_w=0.02),
+    # every token on all 64 experts (the largest k)
+    dict(name="all_experts_every_token", T=300, H=256, E=64, k=64, Im=128, micro=1, dtype=mi.BF16,
+         seed=20, sigma_g=0.02, sigma_w=0.02),
 ]
 
 
@@ -484,6 +487,8 @@ DECODE = [
     dict(T=8, H=2048, E=16, k=16, Im=512, micro=1, seed=33),
     dict(T=16, H=4096, E=64, k=8, Im=256, micro=1, seed=34),
     dict(T=16, H=2048, E=32, k=4, Im=256, micro=2, seed=35, zipf={"s": 1.2, "scale": 6.0, "seed": 35}),
+    # the path's largest routing: 16 tokens on all 64 experts, 1024 routes
+    dict(T=16, H=2048, E=64, k=64, Im=256, micro=1, seed=36),
 ]
 
 
