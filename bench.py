@@ -696,9 +696,10 @@ def main(argv=None):
         torch.cuda.empty_cache()
         d2 = upload(mi.LayerInputs(sp2, base.x, base.wg, base.bias, w1, w2), torch)
         ms2, _, b2 = time_forward(moe, torch, d2, args.steps, args.warmup)
-        extra["denoise_2micro"] = {"ms": round(ms2, 4),
-                                   "tflops": round(expert_flops(sp2) / (ms2 * 1e-3) / 1e12, 2),
-                                   "tokens_per_s": round(sp2.T / (ms2 * 1e-3), 1)}
+        tf2 = expert_flops(sp2) / (ms2 * 1e-3) / 1e12
+        extra["denoise_2micro"] = {"ms": round(ms2, 4), "tflops": round(tf2, 2),
+                                   "tokens_per_s": round(sp2.T / (ms2 * 1e-3), 1),
+                                   "frac_of_bf16_peak": round(tf2 / PEAK_BF16_TFLOPS, 4)}
         log(f"2-micro {ms2:.4f} ms")
         del b2
         # two-dispatch arm: the same 2-micro pack as two one-micro layer calls on
@@ -712,10 +713,12 @@ def main(argv=None):
                   w1=d2["w1"], w2=d2["w2"], sp=sp4)
         ms4, _, b4buf = time_forward(moe, torch, d4, max(3, args.steps // 2), args.warmup)
         c4 = b4buf.views()["counts"].cpu().numpy()
-        extra["skewed_cfg"] = {"ms": round(ms4, 4),
-                               "tflops": round(expert_flops(sp4) / (ms4 * 1e-3) / 1e12, 2),
+        tf4 = expert_flops(sp4) / (ms4 * 1e-3) / 1e12
+        extra["skewed_cfg"] = {"ms": round(ms4, 4), "tflops": round(tf4, 2),
                                "tokens_per_s": round(sp4.T / (ms4 * 1e-3), 1),
-                               "max_load": int(c4.max()), "empty_experts": int((c4 == 0).sum())}
+                               "frac_of_bf16_peak": round(tf4 / PEAK_BF16_TFLOPS, 4),
+                               "max_load": int(c4.max()), "mean_load": round(float(c4.mean()), 1),
+                               "empty_experts": int((c4 == 0).sum())}
         log(f"skewed {ms4:.4f} ms")
         del b4buf
         extra["skewed_cfg"]["two_dispatch_ablation"] = time_two_dispatch(
@@ -729,6 +732,11 @@ def main(argv=None):
     peaks = measure_peaks(moe, torch)
     res["measured_peaks"] = peaks
     res["roofline"]["frac_of_measured_peak"] = round(res["roofline"]["achieved"] / peaks["bf16_mfma_tflops"], 4)
+    res["frac_of_measured_bf16_peak"] = round(res["value"] / peaks["bf16_mfma_tflops"], 4)
+    for lay in res.get("other_layers", {}).values():
+        if "tflops" in lay:
+            lay.setdefault("frac_of_bf16_peak", round(lay["tflops"] / PEAK_BF16_TFLOPS, 4))
+            lay["frac_of_measured_bf16_peak"] = round(lay["tflops"] / peaks["bf16_mfma_tflops"], 4)
     if "decode" in res.get("other_layers", {}):
         dec = res["other_layers"]["decode"]
         dec["frac_of_measured_read_peak"] = round(dec["GB_per_s"] / peaks["hbm_read_GB_per_s"], 4)
