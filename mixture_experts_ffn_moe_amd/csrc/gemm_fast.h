@@ -93,6 +93,18 @@ struct Tile {
   int e, m0, seg_end, nt, valid;
 };
 
+// An optional dense segment run in the same launch after the routed tiles
+// (the shared expert: every token in order, its own weights and output):
+// A rows a[p] for p < rows (row stride H in w13 mode, w in down mode), B the
+// segment's weights (w13: [2w, H], gate rows then up rows; down: [H, w]), C
+// its output (w13: [rows, w]; down: [rows, H]).  rows == 0: none.
+struct Extra {
+  const uint16_t* a;
+  const uint16_t* b;
+  uint16_t* c;
+  int rows, w;
+};
+
 template <bool V>
 struct BoolTag {
   static constexpr bool value = V;
@@ -164,7 +176,7 @@ __device__ __forceinline__ Tile decode(const int32_t* __restrict__ offsets, int 
 // offsets == nullptr is one dense segment of dense_rows rows, as in decode().
 template <int BM, bool EQ = true>
 __device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets, int E, int n_tiles,
-                                            int dense_rows) {
+                                            int dense_rows, int x_rows = 0, int x_ntiles = 0) {
   const int lane = threadIdx.x & 63;
   int off = 0, cnt = 0;
   if (offsets == nullptr) {
@@ -182,22 +194,27 @@ __device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets,
     if (lane >= d) incl += v;
   }
   const int total = __shfl(incl, kWave - 1);
+  // the extra dense segment's tiles follow the routed ones (expert index E)
+  const int x_mt = (x_rows + BM - 1) / BM;
+  const int all = total + x_mt * x_ntiles;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-  const int per = (total + kXcds - 1) / kXcds;
+  const int per = (all + kXcds - 1) / kXcds;
   const int L = xcd * per + slot;
-  const bool ok = slot < per && L < total;
+  const bool ok = slot < per && L < all;
+  const bool xt = L >= total;
   const uint64_t hit = __ballot(lane < E && incl > L);
   const int e = ok && hit ? (__ffsll((long long)hit) - 1) : 0;
   const int e_incl = __shfl(incl, e), e_tiles = __shfl(tiles, e), e_mt = __shfl(mt, e);
   const int e_off = __shfl(off, e), e_cnt = __shfl(cnt, e);
   Tile t;
-  t.valid = (ok && hit) ? 1 : 0;
-  const int local = L - (e_incl - e_tiles);
-  const int mt_safe = e_mt > 0 ? e_mt : 1;
-  const int rows = EQ ? (((e_cnt + mt_safe - 1) / mt_safe + 15) & ~15) : BM;  // <= BM
-  t.e = e;
-  t.m0 = e_off + (t.valid ? (local % mt_safe) * rows : 0);
-  t.seg_end = min(t.m0 + rows, e_off + e_cnt);
+  t.valid = (ok && (hit || xt)) ? 1 : 0;
+  const int local = xt ? L - total : L - (e_incl - e_tiles);
+  const int s_mt = xt ? x_mt : e_mt, s_off = xt ? 0 : e_off, s_cnt = xt ? x_rows : e_cnt;
+  const int mt_safe = s_mt > 0 ? s_mt : 1;
+  const int rows = EQ ? (((s_cnt + mt_safe - 1) / mt_safe + 15) & ~15) : BM;  // <= BM
+  t.e = xt ? E : e;
+  t.m0 = s_off + (t.valid ? (local % mt_safe) * rows : 0);
+  t.seg_end = min(t.m0 + rows, s_off + s_cnt);
   t.nt = t.valid ? local / mt_safe : 0;
   t.valid = __builtin_amdgcn_readfirstlane(t.valid);
   t.e = __builtin_amdgcn_readfirstlane(t.e);
@@ -211,12 +228,22 @@ template <class C, bool PART = true, bool EQ = true>
 __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B, uint16_t* __restrict__ Cout,
-    int H, int E, int k, int Im, int mu, int n_tiles, int dense_rows) {
+    int H, int E, int k, int Im, int mu, int n_tiles, int dense_rows, Extra ex) {
   // A ring (STAGES slots of BM x BK) followed by the B ring (SB slots of BN x BK)
   __shared__ __attribute__((aligned(1024))) uint16_t smem[(C::STAGES * C::BM + C::SB * C::BN) * C::BK];
 
-  const Tile ti = decode_wave<C::BM, EQ>(offsets, E, n_tiles, dense_rows);
+  const int x_ntiles = (C::MODE == kW13) ? ex.w / C::HCOLS : H / C::BN;
+  const Tile ti = decode_wave<C::BM, EQ>(offsets, E, n_tiles, dense_rows, ex.rows, x_ntiles);
   if (!ti.valid) return;
+  // a tile of the extra dense segment: its own A, B, C and width, one micro
+  const bool xt = ti.e == E;
+  if (xt) {
+    A = ex.a;
+    B = ex.b;
+    Cout = ex.c;
+    Im = ex.w;
+    mu = 1;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -244,18 +271,19 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const int c = lpos ^ swz<C::CPR>(row);
     const int p = min(ti.m0 + row, ti.seg_end - 1);
     // A row: x row of route perm[p] (w13), row p of h (down); a dense
-    // segment (no offsets) reads x row p
-    const uint32_t xr = offsets == nullptr ? (uint32_t)p : (uint32_t)(perm[p] / k);
+    // segment (no offsets, or the extra segment) reads row p
+    const uint32_t xr = (offsets == nullptr || xt) ? (uint32_t)p : (uint32_t)(perm[p] / k);
     const uint32_t r = (C::MODE == kW13) ? xr * (uint32_t)H : (uint32_t)p * (uint32_t)lda;
     a_off[i] = (r + c * 8) * 2u;
   }
   const uint16_t* b_base;
   uint32_t b_ld;
+  const int eb = xt ? 0 : ti.e;  // expert block of the weights
   if (C::MODE == kW13) {
-    b_base = B + (size_t)(micro * E + ti.e) * (2 * Im) * H;
+    b_base = B + (size_t)(micro * E + eb) * (2 * Im) * H;
     b_ld = H;
   } else {
-    b_base = B + ((size_t)ti.e * H + n0) * Im;
+    b_base = B + ((size_t)eb * H + n0) * Im;
     b_ld = Im;
   }
   uint32_t b_off[C::B_PER_WAVE];
@@ -478,16 +506,20 @@ inline long long max_m_tiles(long long R, int E, int bm) {
 }
 
 // offsets == nullptr: one dense segment of the T rows (E = k = mu = 1, the
-// shared expert), A rows read in order.
+// shared expert), A rows read in order.  ex: an extra dense segment run
+// after the routed tiles in the same launch (ex.rows == 0: none).
 template <class C, bool PART = true, bool EQ = true>
 hipError_t launch(const void* a, const int32_t* perm, const int32_t* offsets, const void* b,
-                  void* c, int T, int H, int E, int k, int Im, int mu, hipStream_t st) {
+                  void* c, int T, int H, int E, int k, int Im, int mu, hipStream_t st,
+                  Extra ex = Extra{nullptr, nullptr, nullptr, 0, 0}) {
   const int n_tiles = (C::MODE == kW13) ? mu * (Im / C::HCOLS) : H / C::BN;
-  const long long tiles = max_m_tiles((long long)T * k, E, C::BM) * n_tiles;
+  const int x_ntiles = (C::MODE == kW13) ? ex.w / C::HCOLS : H / C::BN;
+  const long long tiles = max_m_tiles((long long)T * k, E, C::BM) * n_tiles +
+                          (long long)((ex.rows + C::BM - 1) / C::BM) * x_ntiles;
   const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
   hipLaunchKernelGGL((grouped_gemm<C, PART, EQ>), dim3(grid), dim3(C::NTHR), 0, st,
                      (const uint16_t*)a, perm, offsets, (const uint16_t*)b, (uint16_t*)c, H, E, k,
-                     Im, mu, n_tiles, T);
+                     Im, mu, n_tiles, T, ex);
   return hipGetLastError();
 }
 

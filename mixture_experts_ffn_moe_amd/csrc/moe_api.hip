@@ -150,15 +150,26 @@ moe_status forward_impl(const Shape& s, const void* x, const float* wg, const fl
   int32_t* hist = (int32_t*)(ws + L.scratch);
   MOE_CHECK(hip_status(moe::launch_route(s, x, wg, bias, logits, ids, w, st, hist)));
   MOE_CHECK(hip_status(moe::launch_permute_hist(s, ids, hist, counts, offsets, perm, inv, st)));
-  MOE_CHECK(hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, st)));
-  MOE_CHECK(hip_status(moe::launch_down(s, h, offsets, w2, y, st)));
   void* ys = nullptr;
-  if (sh) {
-    const Shape d = dense_shape(s, sh->Is);
+  if (sh && s.bf16) {
+    // the shared expert's tiles ride in the routed GEMMs' launches (its w13
+    // alone would leave part of the device idle)
     void* hs = ws + sh->L.hs;
     ys = ws + sh->L.ys;
-    MOE_CHECK(hip_status(moe::launch_w13_swiglu(d, x, nullptr, nullptr, sh->w1s, hs, st)));
-    MOE_CHECK(hip_status(moe::launch_down(d, hs, nullptr, sh->w2s, ys, st)));
+    MOE_CHECK(hip_status(
+        moe::launch_w13_swiglu_with_dense(s, x, perm, offsets, w1, h, sh->w1s, hs, sh->Is, st)));
+    MOE_CHECK(hip_status(
+        moe::launch_down_with_dense(s, h, offsets, w2, y, hs, sh->w2s, ys, sh->Is, st)));
+  } else {
+    MOE_CHECK(hip_status(moe::launch_w13_swiglu(s, x, perm, offsets, w1, h, st)));
+    MOE_CHECK(hip_status(moe::launch_down(s, h, offsets, w2, y, st)));
+    if (sh) {
+      const Shape d = dense_shape(s, sh->Is);
+      void* hs = ws + sh->L.hs;
+      ys = ws + sh->L.ys;
+      MOE_CHECK(hip_status(moe::launch_w13_swiglu(d, x, nullptr, nullptr, sh->w1s, hs, st)));
+      MOE_CHECK(hip_status(moe::launch_down(d, hs, nullptr, sh->w2s, ys, st)));
+    }
   }
   MOE_CHECK(hip_status(moe::launch_finalize(s, y, inv, w, out, st, ys)));
   return MOE_OK;

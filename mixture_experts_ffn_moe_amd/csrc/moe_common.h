@@ -126,6 +126,15 @@ hipError_t launch_w13_swiglu(const Shape& s, const void* x, const int32_t* perm,
 
 hipError_t launch_down(const Shape& s, const void* h, const int32_t* offsets, const void* w2,
                        void* y, hipStream_t st);
+// bf16 only: the routed grouped GEMM and one dense segment of the T tokens in
+// order (the shared expert: weights w1d [2*wd, H] / w2d [H, wd], outputs
+// hd [T, wd] / yd [T, H]) in one launch.
+hipError_t launch_w13_swiglu_with_dense(const Shape& s, const void* x, const int32_t* perm,
+                                        const int32_t* offsets, const void* w1, void* h,
+                                        const void* w1d, void* hd, int wd, hipStream_t st);
+hipError_t launch_down_with_dense(const Shape& s, const void* h, const int32_t* offsets,
+                                  const void* w2, void* y, const void* hd, const void* w2d,
+                                  void* yd, int wd, hipStream_t st);
 
 // ys: the shared expert's output [T, H] added after the routed sum, or nullptr.
 hipError_t launch_finalize(const Shape& s, const void* y, const int32_t* inv, const float* w,

