@@ -174,7 +174,7 @@ __device__ __forceinline__ Tile decode(const int32_t* __restrict__ offsets, int 
 // the end of this tile's rows.  Equal tiles take equal time, so the m-tiles
 // that share an n-tile of weights run side by side and share it in L2.
 // offsets == nullptr is one dense segment of dense_rows rows, as in decode().
-template <int BM, bool EQ = true>
+template <int BM, bool EQ = true, bool XS = false>
 __device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets, int E, int n_tiles,
                                             int dense_rows, int x_rows = 0, int x_ntiles = 0) {
   const int lane = threadIdx.x & 63;
@@ -195,13 +195,13 @@ __device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets,
   }
   const int total = __shfl(incl, kWave - 1);
   // the extra dense segment's tiles follow the routed ones (expert index E)
-  const int x_mt = (x_rows + BM - 1) / BM;
-  const int all = total + x_mt * x_ntiles;
+  const int x_mt = XS ? (x_rows + BM - 1) / BM : 0;
+  const int all = XS ? total + x_mt * x_ntiles : total;
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   const int per = (all + kXcds - 1) / kXcds;
   const int L = xcd * per + slot;
   const bool ok = slot < per && L < all;
-  const bool xt = L >= total;
+  const bool xt = XS && L >= total;
   const uint64_t hit = __ballot(lane < E && incl > L);
   const int e = ok && hit ? (__ffsll((long long)hit) - 1) : 0;
   const int e_incl = __shfl(incl, e), e_tiles = __shfl(tiles, e), e_mt = __shfl(mt, e);
@@ -224,7 +224,7 @@ __device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets,
   return t;
 }
 
-template <class C, bool PART = true, bool EQ = true>
+template <class C, bool PART = true, bool EQ = true, bool XS = false>
 __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B, uint16_t* __restrict__ Cout,
@@ -232,11 +232,13 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
   // A ring (STAGES slots of BM x BK) followed by the B ring (SB slots of BN x BK)
   __shared__ __attribute__((aligned(1024))) uint16_t smem[(C::STAGES * C::BM + C::SB * C::BN) * C::BK];
 
-  const int x_ntiles = (C::MODE == kW13) ? ex.w / C::HCOLS : H / C::BN;
-  const Tile ti = decode_wave<C::BM, EQ>(offsets, E, n_tiles, dense_rows, ex.rows, x_ntiles);
+  // XS: the launch has an extra dense segment (a separate instantiation, so
+  // the routed-only kernel carries none of its tile logic)
+  const int x_ntiles = XS ? ((C::MODE == kW13) ? ex.w / C::HCOLS : H / C::BN) : 0;
+  const Tile ti = decode_wave<C::BM, EQ, XS>(offsets, E, n_tiles, dense_rows, ex.rows, x_ntiles);
   if (!ti.valid) return;
   // a tile of the extra dense segment: its own A, B, C and width, one micro
-  const bool xt = ti.e == E;
+  const bool xt = XS && ti.e == E;
   if (xt) {
     A = ex.a;
     B = ex.b;
@@ -517,9 +519,14 @@ hipError_t launch(const void* a, const int32_t* perm, const int32_t* offsets, co
   const long long tiles = max_m_tiles((long long)T * k, E, C::BM) * n_tiles +
                           (long long)((ex.rows + C::BM - 1) / C::BM) * x_ntiles;
   const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
-  hipLaunchKernelGGL((grouped_gemm<C, PART, EQ>), dim3(grid), dim3(C::NTHR), 0, st,
-                     (const uint16_t*)a, perm, offsets, (const uint16_t*)b, (uint16_t*)c, H, E, k,
-                     Im, mu, n_tiles, T, ex);
+  if (ex.rows > 0)
+    hipLaunchKernelGGL((grouped_gemm<C, PART, EQ, true>), dim3(grid), dim3(C::NTHR), 0, st,
+                       (const uint16_t*)a, perm, offsets, (const uint16_t*)b, (uint16_t*)c, H, E, k,
+                       Im, mu, n_tiles, T, ex);
+  else
+    hipLaunchKernelGGL((grouped_gemm<C, PART, EQ, false>), dim3(grid), dim3(C::NTHR), 0, st,
+                       (const uint16_t*)a, perm, offsets, (const uint16_t*)b, (uint16_t*)c, H, E, k,
+                       Im, mu, n_tiles, T, ex);
   return hipGetLastError();
 }
 
