@@ -535,6 +535,12 @@ SHARED = [
     dict(name="f32_two_micro", T=200, H=256, E=8, k=2, Im=128, micro=2, dtype=mi.F32, seed=14),
     dict(name="bf16_one_row_tail", T=321, H=768, E=4, k=1, Im=384, micro=1, dtype=mi.BF16, seed=42,
          sigma_g=0.02, sigma_w=0.02),
+    # shared widths other than the routed width I (its down tiles then run a
+    # different K from the routed tiles in the same launch)
+    dict(name="bf16_narrow_shared", T=700, H=512, E=8, k=2, Im=256, micro=2, dtype=mi.BF16, seed=43,
+         sigma_g=0.02, sigma_w=0.02, Is=128),
+    dict(name="bf16_wide_shared", T=300, H=256, E=6, k=2, Im=128, micro=1, dtype=mi.BF16, seed=44,
+         sigma_g=0.02, sigma_w=0.02, Is=640),
 ]
 
 
@@ -550,11 +556,13 @@ def test_shared_expert_layer(m, case):
     moe_finalize_shared after the routed steps) against the one call, bit
     for bit (same kernels, same order)."""
     from mixture_experts_ffn_moe_amd import MoELayerBuffers
-    sp = small_spec(case)
-    say(f"[parity] shared expert {case['name']}: T={sp.T} H={sp.H} E={sp.E} k={sp.k} I={sp.I}")
+    c = dict(case)
+    Is_req = c.pop("Is", None)
+    sp = small_spec(c)
     inp = mi.make_layer(sp)
-    w1s, w2s = mi.make_shared(sp)
+    w1s, w2s = mi.make_shared(sp, Is_req)
     Is = w2s.shape[1]
+    say(f"[parity] shared expert {case['name']}: T={sp.T} H={sp.H} E={sp.E} k={sp.k} I={sp.I} Is={Is}")
     ref = o.forward_shared(inp, w1s, w2s)
     d = device_inputs(inp)
     dw1s, dw2s = shared_device(sp, w1s, w2s)
@@ -587,22 +595,27 @@ SHARED_DECODE = [
     dict(T=16, H=4096, E=64, k=8, Im=256, micro=1, seed=53),
     # ~5300 column units: more than one unit per wave in the w13 work split
     dict(T=16, H=2048, E=32, k=8, Im=1280, micro=2, seed=54),
+    # a shared width other than the routed width
+    dict(T=8, H=2048, E=16, k=4, Im=256, micro=1, seed=55, Is=768),
 ]
 
 
 @pytest.mark.parametrize("case", SHARED_DECODE,
-                         ids=[f"T{c['T']}_E{c['E']}_k{c['k']}_mu{c['micro']}" for c in SHARED_DECODE])
+                         ids=[f"T{c['T']}_E{c['E']}_k{c['k']}_mu{c['micro']}" + (f"_Is{c['Is']}" if "Is" in c else "")
+                              for c in SHARED_DECODE])
 def test_shared_expert_decode_path(m, case):
     """moe_forward_shared with T <= 16 streams the shared expert's weights in
     the decode kernels: routing and the shared activations hs are the same
     bits as the token path's, the output meets the bar against the oracle
     and against the token path."""
     from mixture_experts_ffn_moe_amd import MoELayerBuffers
-    sp = mi.custom_spec(dtype=mi.BF16, name="decode", sigma_g=0.02, sigma_w=0.02, **case)
-    say(f"[parity] shared expert decode path T={sp.T} H={sp.H} E={sp.E} k={sp.k} I={sp.I}")
+    c = dict(case)
+    Is_req = c.pop("Is", None)
+    sp = mi.custom_spec(dtype=mi.BF16, name="decode", sigma_g=0.02, sigma_w=0.02, **c)
     inp = mi.make_layer(sp)
-    w1s, w2s = mi.make_shared(sp)
+    w1s, w2s = mi.make_shared(sp, Is_req)
     Is = w2s.shape[1]
+    say(f"[parity] shared expert decode path T={sp.T} H={sp.H} E={sp.E} k={sp.k} I={sp.I} Is={Is}")
     ref = o.forward_shared(inp, w1s, w2s)
     d = device_inputs(inp)
     dw1s, dw2s = shared_device(sp, w1s, w2s)
