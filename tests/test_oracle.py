@@ -285,14 +285,17 @@ def test_tiny_layer_matches_dense_bruteforce():
 @pytest.mark.parametrize("cfg", [
     dict(T=40, H=48, E=8, k=2, Im=16, micro=1, seed=21),
     dict(T=25, H=64, E=6, k=3, Im=8, micro=2, seed=22),
+    dict(T=30, H=32, E=5, k=2, Im=8, micro=1, seed=23, Is=24),  # shared width != routed width
 ])
 def test_shared_expert_matches_dense_bruteforce(cfg):
     """The layer with its shared expert against the dense brute force with
     the shared expert as one more expert whose coefficient is 1 for every
     token (brute_dense's own FFN code, not the oracle's expert_ffn)."""
+    cfg = dict(cfg)
+    Is = cfg.pop("Is", None)
     sp = mi.custom_spec(dtype=mi.F32, **cfg)
     inp = mi.make_layer(sp)
-    w1s, w2s = mi.make_shared(sp)
+    w1s, w2s = mi.make_shared(sp, Is)
     r = o.forward_shared(inp, w1s, w2s)
     w13s, downs = _unsharded(inp)
     ids = np.concatenate([r["ids"], np.full((sp.T, 1), sp.E, dtype=np.int32)], axis=1)
