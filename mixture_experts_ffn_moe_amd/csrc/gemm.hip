@@ -134,20 +134,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 // w13: 320 rows x (128 gate + 128 up) B-rows, BK 64, 8 waves of 80 x 128
 // (4 x 2 waves: 13 fragment reads per 40 MFMAs instead of 14 for 160 x 64,
 // and a partial tile's padded rows skipped in 80-row blocks; 3% faster, h
-// bit-identical); down: 256 rows x 256 output columns, 8 waves of 128 x 64
-// (2 x 4; 4 x 2 was 1% slower there).  BK 64 keeps
+// bit-identical); down: 320 rows x 256 output columns, 8 waves of 80 x 128
+// (5% faster than 256 rows in 2 x 4 waves of 128 x 64; 320 rows in 2 x 4
+// were not).  BK 64 keeps
 // every row copy a full 128-byte line (64-byte pieces halve the copy rate).
 // Two waves per SIMD are needed for the 16x16x32 MFMA to issue at full rate.
 //  * 320-row tiles cover an expert of up to 640 routes in two m-tiles (256-row
 //    tiles need three once an expert passes 512, and each extra m-tile streams
 //    the expert's weight tile again): 2.3% faster for w13 at the near-uniform
-//    loads of the denoise layer.  For down, 256 and 320 rows are within 2%.
+//    loads of the denoise layer (6% with the 4 x 2 waves).
 //  * Two weight slots for both.  A third slot raised w13's fabric reads by
 //    16% for no gain; for down it helped while the epilogue stored 32-byte
 //    pieces, and is 2% slower since the epilogue goes through LDS (down's
-//    256-row output tile then leaves in two passes of 128 rows).
+//    output tile leaves in one pass per 80-row block of waves).
 using W13Cfg = fast::Cfg<fast::kW13, 320, 256, 64, 2, 4, 2, 2>;
-using DownCfg = fast::Cfg<fast::kDown, 256, 256, 64, 2, 2, 4, 2>;
+using DownCfg = fast::Cfg<fast::kDown, 320, 256, 64, 2, 4, 2, 2>;
 
 
 inline unsigned grid_size(long long tiles) {
