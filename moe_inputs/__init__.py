@@ -91,6 +91,7 @@ class LayerSpec:
     sigma_w: float = 0.02
     zipf_bias: Optional[dict] = None   # {"s": 1.2, "scale": 2.0, "seed": 4}
     note: str = ""
+    renormalize: bool = True  # routing weights renormalised over the k selected experts
 
     @property
     def I(self) -> int:
@@ -242,8 +243,8 @@ def make_layer(sp, weights: bool = True) -> LayerInputs:
 
 
 def custom_spec(T, H, E, k, Im, micro=1, dtype=F32, seed=100, sigma_g=0.1, sigma_w=0.05,
-                zipf=None, name="custom") -> LayerSpec:
+                zipf=None, name="custom", renormalize=True) -> LayerSpec:
     """A layer of arbitrary (small) shape for tests."""
     return LayerSpec(name, T=T, H=H, E=E, k=k, Im=Im, micro=micro, dtype=dtype,
                      x_seed=seed, layer_seed=seed + 1, sigma_g=sigma_g, sigma_w=sigma_w,
-                     zipf_bias=zipf)
+                     zipf_bias=zipf, renormalize=renormalize)

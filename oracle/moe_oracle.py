@@ -17,9 +17,11 @@ What is computed, and where the pages state it:
   the bias added in float64, and the sum rounded once to fp32.
 * Gating: softmax over all experts, the k largest logits (ties to the lower
   expert index, slot j = j-th in that order), and weights renormalised over the
-  selected experts.  The pages only say the router yields expert ids and routing
-  scores of shape [num_tokens, top_k] (hybrid parallelism, section 6.1); k,
-  softmax and renormalisation are the workload's definition.
+  selected experts (or, with renormalisation off, the softmax probabilities of
+  the selected experts as they are).  The pages only say the router yields
+  expert ids and routing scores of shape [num_tokens, top_k] (hybrid
+  parallelism, section 6.1); k, softmax and renormalisation are the workload's
+  definition.
 * Route permutation: the flattened expert ids sorted by expert (stably, so
   each expert's rows keep token order), giving permuted_to_expanded; per-expert
   offsets from a bincount and a cumulative sum (hybrid parallelism, section 6.1;
@@ -90,11 +92,28 @@ def router_logits(x32: np.ndarray, wg: np.ndarray, bias: Optional[np.ndarray]) -
     return L
 
 
-def logits_near_midpoint(x32, wg, bias, rel: float = 2.0 ** -40) -> np.ndarray:
+def summation_bound_rel(n_terms: int) -> float:
+    """2 * gamma_{n-1}, gamma_m = m u / (1 - m u), u = 2^-53: twice the
+    worst-case error of a float64 sum of n exactly known terms taken in any
+    order of pairwise additions, relative to the sum of their magnitudes (the
+    standard bound of recursive summation, e.g. Higham, "Accuracy and
+    Stability of Numerical Algorithms", section 4.2).  Two float64 sums of the
+    same n terms in different orders can differ by at most this much."""
+    m = max(int(n_terms) - 1, 0)
+    u = 2.0 ** -53
+    return 2.0 * m * u / (1.0 - m * u)
+
+
+def logits_near_midpoint(x32, wg, bias, rel: Optional[float] = None) -> np.ndarray:
     """Flag logits whose float64 sum lies so close to an fp32 rounding
     midpoint that another float64 summation order could round it the other
-    way.  Such logits are not pinned bit for bit (the bound is a generous
-    multiple of the float64 summation error over 4096-term sums)."""
+    way: within rel * sum_h |x[t,h] wg[e,h]| (+ |bias[e]|) of a midpoint, rel
+    by default the two-order bound of summation_bound_rel over the H products
+    and the bias.  Every other logit has one fp32 value whatever float64
+    order the sum is taken in, so it is pinned bit for bit."""
+    H = x32.shape[1]
+    if rel is None:
+        rel = summation_bound_rel(H + (1 if bias is not None else 0))
     L64 = router_logits_f64(x32, wg, bias)
     L32 = L64.astype(np.float32)
     up = np.nextafter(L32, np.float32(np.inf)).astype(np.float64)
@@ -118,15 +137,18 @@ def select_topk(L: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k].astype(np.int32)
 
 
-def topk_weights(L: np.ndarray, ids: np.ndarray) -> np.ndarray:
-    """Softmax over all experts, then the selected probabilities divided by
-    their sum; computed in float64 and rounded once to fp32."""
+def topk_weights(L: np.ndarray, ids: np.ndarray, renormalize: bool = True) -> np.ndarray:
+    """Softmax over all experts at the selected ones, in float64, rounded
+    once to fp32; with renormalize, divided by their sum first (so the k
+    weights of a token sum to 1)."""
     L64 = L.astype(np.float64)
     z = L64 - L64.max(axis=1, keepdims=True)
     p = np.exp(z)
     p /= p.sum(axis=1, keepdims=True)
     sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    return (sel / sel.sum(axis=1, keepdims=True)).astype(np.float32)
+    if renormalize:
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    return sel.astype(np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -205,7 +227,7 @@ def route(inp: LayerInputs) -> dict:
     x32 = widen(inp.x, sp.dtype)
     L = router_logits(x32, inp.wg, inp.bias)
     ids = select_topk(L, sp.k)
-    w = topk_weights(L, ids)
+    w = topk_weights(L, ids, sp.renormalize)
     counts = expert_counts(ids, sp.E)
     offsets = expert_offsets(counts)
     perm, inv = route_permutation(ids)

@@ -11,7 +11,7 @@ from oracle import moe_oracle as m
 
 _orig = {name: getattr(m, name) for name in (
     "router_logits_f64", "select_topk", "topk_weights", "route_permutation", "silu", "expert_ffn",
-    "finalize")}
+    "finalize", "logits_near_midpoint")}
 
 
 def _gate_up_swap(xr, w1s, w2s, Im):
@@ -40,12 +40,17 @@ def _upper_index_ties(L, k):
     return (E - 1 - order[:, :k]).astype(np.int32)
 
 
-def _no_renormalisation(L, ids):
+def _no_renormalisation(L, ids, renormalize=True):
     L64 = L.astype(np.float64)
     z = L64 - L64.max(axis=1, keepdims=True)
     p = np.exp(z)
     p /= p.sum(axis=1, keepdims=True)
     return np.take_along_axis(p, ids.astype(np.int64), axis=1).astype(np.float32)
+
+
+def _renormalise_always(L, ids, renormalize=True):
+    # the flag ignored: weights renormalised even when it is off
+    return _orig["topk_weights"](L, ids, True)
 
 
 def _swapped_perm_inv(ids):
@@ -72,17 +77,35 @@ def _dropped_hidden_term(x32, wg, bias):
     return _orig["router_logits_f64"](x32[:, :-1], wg[:, :-1], bias)
 
 
+def _guard_overflags(x32, wg, bias, rel=None):
+    # a slip in the midpoint bound (2^-20 for 2^-40): every logit excused
+    return _orig["logits_near_midpoint"](x32, wg, bias, rel=2.0 ** -20)
+
+
+def _guard_fixed_bound(x32, wg, bias, rel=None):
+    # the bound of 4096-term sums used whatever the number of terms
+    return _orig["logits_near_midpoint"](x32, wg, bias, rel=2.0 ** -40)
+
+
+def _guard_flags_nothing(x32, wg, bias, rel=None):
+    return np.zeros((x32.shape[0], wg.shape[0]), dtype=bool)
+
+
 MUTANTS = {
     "gate_up_swap": ("expert_ffn", _gate_up_swap),
     "unstable_sort": ("route_permutation", _unstable_sort),
     "dropped_bias": ("router_logits_f64", _dropped_bias),
     "upper_index_ties": ("select_topk", _upper_index_ties),
     "no_renormalisation": ("topk_weights", _no_renormalisation),
+    "renormalise_always": ("topk_weights", _renormalise_always),
     "swapped_perm_inv": ("route_permutation", _swapped_perm_inv),
     "wrong_finalize_slot": ("finalize", _wrong_finalize_slot),
     "silu_sign": ("silu", _silu_sign),
     "dropped_micro": ("expert_ffn", _dropped_micro),
     "dropped_hidden_term": ("router_logits_f64", _dropped_hidden_term),
+    "guard_overflags": ("logits_near_midpoint", _guard_overflags),
+    "guard_fixed_bound": ("logits_near_midpoint", _guard_fixed_bound),
+    "guard_flags_nothing": ("logits_near_midpoint", _guard_flags_nothing),
 }
 
 

@@ -53,6 +53,84 @@ def test_router_logits_match_exactly_rounded_sum():
                 assert np.float32(s) == L[t, e], (t, e)
 
 
+def _f32_of_fraction(F):
+    """The fp32 value nearest to the exact rational F, ties to the even
+    significand: chosen among the fp32 neighbours of float(F) by exact
+    rational distance (no double rounding through float64)."""
+    c = np.float32(float(F))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - F), int(np.float32(v).view(np.uint32)) & 1))
+
+
+def _dyadic_router(terms):
+    """One token, one expert, H = len(terms) products x_h * w_h = terms[h],
+    each term a power of two times +-1 split as x = 2^a, w = +-2^b."""
+    x = np.array([[2.0 ** (math.frexp(abs(t))[1] // 2)] for t in terms], np.float64).T
+    w = (np.array(terms, np.float64) / x[0])[None, :]
+    return x.astype(np.float32), w.astype(np.float32)
+
+
+def test_midpoint_guard_flags_exact_midpoint():
+    """1 + 2^-24 is exactly halfway between the fp32 neighbours 1 and
+    1 + 2^-23: its rounding depends on the last bit of any float64 sum, so
+    the guard must flag it (and its negative, and 3 * 2^-30 + 2^-53, the
+    midpoint above 3 * 2^-30 in a binade of ulp 2^-52); 1.5 is an fp32 value,
+    half an ulp from either midpoint, and must not be flagged."""
+    for terms, want in (([1.0, 2.0 ** -24], True), ([-1.0, -(2.0 ** -24)], True),
+                        ([1.0, 0.5], False), ([3.0 * 2.0 ** -30, 2.0 ** -53], True)):
+        x, w = _dyadic_router(terms)
+        assert float((x.astype(np.float64) @ w.astype(np.float64).T)[0, 0]) == sum(terms)
+        assert bool(o.logits_near_midpoint(x, w, None)[0, 0]) is want, terms
+
+
+def test_midpoint_guard_bound_scales_with_terms():
+    """Three exact terms 1 + 2^-24 + d: the sum is d from a midpoint and the
+    bound of two float64 orders over three terms is 2 * 2u * (1 + ...) ~
+    2^-51 of the magnitude.  d = 2^-51 must be flagged; d = 2^-50 and 2^-48
+    (well inside a fixed 2^-40, which the bound reaches only at H ~ 4096)
+    must not."""
+    assert o.summation_bound_rel(3) == pytest.approx(2.0 ** -51, rel=1e-12)
+    assert o.summation_bound_rel(4097) == pytest.approx(2.0 ** -40, rel=1e-12)
+    for d, want in ((2.0 ** -51, True), (2.0 ** -50, False), (2.0 ** -48, False)):
+        x, w = _dyadic_router([1.0, 2.0 ** -24, d])
+        assert bool(o.logits_near_midpoint(x, w, None)[0, 0]) is want, d
+    # a bias term is one more summand: 2^-51 away is still inside the bound
+    x, w = _dyadic_router([1.0, 2.0 ** -24])
+    assert bool(o.logits_near_midpoint(x, w, np.array([2.0 ** -51], np.float32))[0, 0])
+    assert not o.logits_near_midpoint(x, w, np.array([2.0 ** -47], np.float32))[0, 0]
+
+
+def test_unflagged_logits_are_the_exact_sum_correctly_rounded():
+    """What the guard leaves unflagged is pinned: there, the oracle's logit
+    is the exact rational sum rounded once to fp32 (round to nearest even),
+    computed here without float64.  Activations are bf16 of N(0,1), router
+    rows fp32 of N(0, 0.1), plus rows built to sit near midpoints.  The
+    guard flags only a small fraction of random logits."""
+    rng = np.random.default_rng(8)
+    T, H, E = 12, 96, 10
+    x = mi.bf16_bits_to_f32(mi.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    wg = (rng.standard_normal((E, H)) * 0.1).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.5).astype(np.float32)
+    # token 0 / expert 0: 1 + 2^-24 + 2^-60 exactly (a midpoint plus a hair)
+    x[0] = 0.0
+    wg[0] = 0.0
+    x[0, :3] = [1.0, 2.0 ** -12, 2.0 ** -30]
+    wg[0, :3] = [1.0, 2.0 ** -12, 2.0 ** -30]
+    b[0] = 0.0
+    L = o.router_logits(x, wg, b)
+    flags = o.logits_near_midpoint(x, wg, b)
+    assert flags[0, 0]
+    assert flags.mean() < 0.02
+    checked = 0
+    for t in range(T):
+        for e in range(E):
+            exact = sum(Fraction(float(x[t, h])) * Fraction(float(wg[e, h])) for h in range(H)) + Fraction(float(b[e]))
+            if not flags[t, e]:
+                assert L[t, e].view(np.uint32) == _f32_of_fraction(exact).view(np.uint32), (t, e)
+                checked += 1
+    assert checked >= T * E - 3
+
+
 def test_router_bias_shifts_logits():
     x = np.ones((2, 4), np.float32)
     wg = np.zeros((3, 4), np.float32)
@@ -123,6 +201,14 @@ def test_topk_weights_properties():
     w = o.topk_weights(L, ids)
     ref = softmax(L.astype(np.float64), axis=1)
     np.testing.assert_allclose(w, np.take_along_axis(ref, ids, axis=1), rtol=1e-6)
+    # renormalisation off: scipy's softmax over all experts at the selected
+    # ones, for every k (summing to less than 1 below k = E)
+    for k in (1, 3, 16):
+        ids = o.select_topk(L, k)
+        w = o.topk_weights(L, ids, renormalize=False)
+        np.testing.assert_allclose(w, np.take_along_axis(ref, ids, axis=1), rtol=1e-6)
+        if k < 16:
+            assert np.all(w.sum(axis=1) < 1.0)
     # two selected experts: closed form sigmoid of the logit gap
     L = np.array([[0.3, -1.2, 5.0]], np.float32)
     ids = o.select_topk(L, 2)
