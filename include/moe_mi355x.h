@@ -24,7 +24,8 @@
  *  - Arguments are validated on the host first.  On any error nothing is
  *    enqueued and no output is touched.  Device data (finite logits and
  *    weights) is a documented precondition, not checked.
- *  - A shape with T == 0 is valid: the call validates and enqueues nothing.
+ *  - A shape with T == 0 is valid: the call validates and enqueues nothing,
+ *    except moe_permute, which writes zero counts and offsets.
  *
  * Notation: T tokens, H hidden size, E experts, k routes per token,
  * Im intermediate columns per micro-shard, mu = micro_count, R = T*k routes.
@@ -63,6 +64,8 @@ typedef struct {
   int32_t Im;           /* intermediate columns per micro-shard */
   int32_t micro_count;  /* micro-shards stored micro-major, >= 1 */
   int32_t dtype;        /* moe_dtype */
+  int32_t renormalize;  /* 1: routing weights renormalised to sum 1 over the k selected
+                           experts; 0: the softmax over all E experts at the selected ones */
 } moe_shape;
 
 /* Byte offsets of the intermediates inside a moe_forward workspace (each
@@ -99,7 +102,8 @@ moe_status moe_get_workspace_layout(const moe_shape* shape, moe_workspace_layout
  *     products and sum in fp64, one rounding to fp32.
  *   topk_ids[t, j]: the j-th expert in (logit descending, expert ascending)
  *     order, -0.0 equal to +0.0; topk_w[t, j] = softmax over all experts at
- *     the selected ones, renormalised to sum 1 over the k selected.
+ *     the selected ones (computed in fp64, rounded once), renormalised to sum
+ *     1 over the k selected when shape->renormalize is 1.
  * Outputs: logits [T, E] fp32, topk_ids [T, k] int32, topk_w [T, k] fp32. */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* wg, const float* bias,
                      float* logits, int32_t* topk_ids, float* topk_w, void* stream);
@@ -113,6 +117,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* wg, con
  *   If both x and permuted_x are non-NULL, also writes the gathered input
  *   permuted_x[p, :] = x[perm[p] / k, :] (dtype, [R, H]); the one-call path
  *   never materialises it (the w13 GEMM gathers rows itself).
+ * With T == 0 only counts and offsets are written (all zero); the other
+ * pointers may then be NULL.
  * topk_ids must hold experts in [0, E) (as moe_route writes them); an id
  * outside that range is clamped into it, so every write stays in bounds and
  * perm is still a permutation, but the result is then unspecified.

@@ -41,7 +41,7 @@ class MoeError(RuntimeError):
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("Im", ctypes.c_int32), ("micro_count", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("renormalize", ctypes.c_int32)]
 
 
 class MoeWorkspaceLayout(ctypes.Structure):
@@ -105,9 +105,9 @@ def status_string(code: int) -> str:
     return lib.moe_status_string(code).decode()
 
 
-def make_shape(T, H, E, k, Im, micro_count=1, dtype="bf16") -> MoeShape:
+def make_shape(T, H, E, k, Im, micro_count=1, dtype="bf16", renormalize=True) -> MoeShape:
     d = {"bf16": MOE_BF16, "f32": MOE_F32, MOE_BF16: MOE_BF16, MOE_F32: MOE_F32}[dtype]
-    return MoeShape(T, H, E, k, Im, micro_count, d)
+    return MoeShape(T, H, E, k, Im, micro_count, d, int(bool(renormalize)))
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -138,8 +138,8 @@ struct RouteLds {
 };
 
 __device__ __forceinline__ void route_finish(
-    const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k, bool out,
-    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ topw,
+    const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k, bool renorm,
+    bool out, float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ topw,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, int32_t* __restrict__ active, RouteLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -181,7 +181,8 @@ __device__ __forceinline__ void route_finish(
       const uint64_t chosen = __ballot(taken);
       if (lane == 0) S.sel[t] = chosen;
       const double ex = (lane < k) ? exp((double)mine - (double)first) : 0.0;
-      const double s = wave_sum_f64(ex);
+      const double s =
+          wave_sum_f64(renorm ? ex : (lane < E ? exp((double)S.lg[t][lane] - (double)first) : 0.0));
       if (out && lane < k) topw[(size_t)t * k + lane] = (float)(ex / s);
     }
   }
@@ -291,11 +292,11 @@ __global__ __launch_bounds__(kW13Waves * 64) void decode_w13(
     uint16_t* __restrict__ h, const uint16_t* __restrict__ w1s, int Is, uint16_t* __restrict__ hs,
     float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ topw,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets_out, int32_t* __restrict__ perm_out,
-    int32_t* __restrict__ inv, int32_t* __restrict__ active_out) {
+    int32_t* __restrict__ inv, int32_t* __restrict__ active_out, int renorm) {
   static_assert(kW13Waves * 64 == kDecT * kMaxExperts, "routing: one thread per (token, expert)");
   __shared__ __attribute__((aligned(16))) char buf[kW13Waves][2][2048];  // per wave: gate, up
   __shared__ RouteLds rs;
-  route_finish(partial, bias, T, E, k, blockIdx.x == 0, logits, ids, topw, counts, offsets_out, perm_out,
+  route_finish(partial, bias, T, E, k, renorm != 0, blockIdx.x == 0, logits, ids, topw, counts, offsets_out, perm_out,
                inv, active_out, rs);
   const int* active = rs.act;
   const int* offsets = rs.off;
@@ -514,7 +515,7 @@ hipError_t launch_decode(const Shape& s, const void* x, const float* wg, const f
   const int Is = shared ? shared->Is : 0;
   hipLaunchKernelGGL(decode_w13, dim3(kW13Blocks), dim3(kW13Waves * 64), 0, st, (const uint16_t*)x,
                      partial, bias, (const uint16_t*)w1, s.T, s.H, s.E, s.k, s.Im, s.mu, (uint16_t*)h,
-                     w1s, Is, hs, logits, ids, w, counts, offsets, perm, inv, active);
+                     w1s, Is, hs, logits, ids, w, counts, offsets, perm, inv, active, (int)s.renorm);
   hipLaunchKernelGGL(decode_down_finalize, dim3(s.H / 16), dim3(kDownWaves * 64), 0, st, (const uint16_t*)h,
                      perm, offsets, active, w, (const uint16_t*)w2, s.T, s.H, s.E, s.k, s.Im,
                      s.mu, (uint16_t*)out, (const uint16_t*)hs, w2s, Is);

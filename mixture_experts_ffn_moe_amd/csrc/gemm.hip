@@ -66,8 +66,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
   const float* a_src;
   {
     const int p = min(ti.m0 + lr, ti.seg_end - 1);
-    const int xr = offsets == nullptr ? p : perm[p] / k;  // dense segment: x row p
-    a_src = (MODE == kW13) ? A + (size_t)xr * H : A + (size_t)p * lda;
+    if constexpr (MODE == kW13) {
+      const int xr = offsets == nullptr ? p : perm[p] / k;  // dense segment: x row p
+      a_src = A + (size_t)xr * H;
+    } else {
+      a_src = A + (size_t)p * lda;  // down: row p of h (no perm is passed)
+    }
   }
   size_t b_base;
   if (MODE == kW13) {

@@ -73,7 +73,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // and barrier themselves before reading the destination.
 __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
 // Workgroup barrier for the k loop.  __syncthreads() carries a memory fence
@@ -272,10 +272,16 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const int row = (wave + C::NW * i) * C::RPI + lrow;
     const int c = lpos ^ swz<C::CPR>(row);
     const int p = min(ti.m0 + row, ti.seg_end - 1);
-    // A row: x row of route perm[p] (w13), row p of h (down); a dense
-    // segment (no offsets, or the extra segment) reads row p
-    const uint32_t xr = (offsets == nullptr || xt) ? (uint32_t)p : (uint32_t)(perm[p] / k);
-    const uint32_t r = (C::MODE == kW13) ? xr * (uint32_t)H : (uint32_t)p * (uint32_t)lda;
+    // A row: x row of route perm[p] (w13), row p of h (down: no perm is
+    // passed, and none is read); a dense segment (no offsets, or the extra
+    // segment) reads row p
+    uint32_t r;
+    if constexpr (C::MODE == kW13) {
+      const uint32_t xr = (offsets == nullptr || xt) ? (uint32_t)p : (uint32_t)(perm[p] / k);
+      r = xr * (uint32_t)H;
+    } else {
+      r = (uint32_t)p * (uint32_t)lda;
+    }
     a_off[i] = (r + c * 8) * 2u;
   }
   const uint16_t* b_base;

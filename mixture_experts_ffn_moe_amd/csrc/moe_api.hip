@@ -28,6 +28,7 @@ moe_status check_shape(const moe_shape* sh, Shape* out) {
     return MOE_ERR_INVALID_ARG;
   if (s.k > s.E) return MOE_ERR_INVALID_ARG;
   if (s.dtype != MOE_F32 && s.dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s.renormalize != 0 && s.renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (s.E > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s.H % 256 != 0 || s.Im % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const long long R = (long long)s.T * s.k;
@@ -42,6 +43,7 @@ moe_status check_shape(const moe_shape* sh, Shape* out) {
   if (out) {
     out->T = s.T; out->H = s.H; out->E = s.E; out->k = s.k; out->Im = s.Im;
     out->mu = s.micro_count; out->bf16 = (s.dtype == MOE_BF16);
+    out->renorm = (s.renormalize != 0);
   }
   return MOE_OK;
 }
@@ -224,9 +226,8 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_ids, int32_t*
   MOE_CHECK(check_shape(shape, &s));
   MOE_CHECK(check_ptr(counts)); MOE_CHECK(check_ptr(offsets));
   if ((x == nullptr) != (permuted_x == nullptr)) return MOE_ERR_INVALID_ARG;
-  if (s.T == 0) {
-    return MOE_OK;
-  }
+  if (s.T == 0)  // no routes: zero counts and offsets, nothing else
+    return hip_status(moe::launch_permute(s, topk_ids, counts, offsets, perm, inv, (hipStream_t)stream));
   MOE_CHECK(check_ptr(topk_ids)); MOE_CHECK(check_ptr(perm)); MOE_CHECK(check_ptr(inv));
   if (x != nullptr) { MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(permuted_x)); }
   hipStream_t st = (hipStream_t)stream;

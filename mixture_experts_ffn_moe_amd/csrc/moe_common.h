@@ -95,6 +95,7 @@ template <> struct Elem<uint16_t> {
 struct Shape {
   int T, H, E, k, Im, mu;
   bool bf16;
+  bool renorm;  // routing weights renormalised over the k selected experts
   long long R() const { return (long long)T * k; }
 };
 

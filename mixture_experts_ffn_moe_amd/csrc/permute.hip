@@ -194,9 +194,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x,
 
 }  // namespace
 
+// An empty batch: every count and offset is zero (offsets[E] = R = 0).  A
+// kernel rather than a memset, so a captured graph holds only kernels.
+__global__ __launch_bounds__(kWave * 2) void zero_counts_kernel(int E, int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets) {
+  const int e = threadIdx.x;
+  if (e < E) counts[e] = 0;
+  if (e <= E) offsets[e] = 0;
+}
+
 hipError_t launch_permute(const Shape& s, const int32_t* ids, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* inv, hipStream_t st) {
   const int R = (int)s.R();
+  if (R == 0) {
+    hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(kWave * 2), 0, st, s.E, counts, offsets);
+    return hipGetLastError();
+  }
   const long long even = ((long long)R + kMaxBlocks - 1) / kMaxBlocks;
   const int chunk = (int)std::max<long long>(kMinChunk, (even + 63) / 64 * 64);
   const unsigned blocks = (unsigned)(((long long)R + chunk - 1) / chunk);

@@ -1,4 +1,5 @@
-// Router logits, top-k selection and renormalised softmax weights.
+// Router logits, top-k selection and softmax weights (renormalised over the
+// selected experts, or not).
 //
 // The router is replicated and runs in fp32 with fp32 weights
 // ("HunyuanImage-3.0 on CANN NPU", section 5.2); it yields expert ids and
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
                                                     int E, int k, float* __restrict__ logits,
                                                     int32_t* __restrict__ ids,
                                                     float* __restrict__ topw,
-                                                    int32_t* __restrict__ hist) {
+                                                    int32_t* __restrict__ hist, int renorm) {
   __shared__ double part[kHParts][kTokTile][kMaxExperts + 1];
   __shared__ float lg[kTokTile][kMaxExperts];
   __shared__ int hcnt[kMaxExperts];
@@ -174,10 +175,11 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
         if (hist != nullptr) atomicAdd(&hcnt[win], 1);
       }
     }
-    // weights: softmax restricted to the selected experts (the full softmax
-    // denominator cancels in the renormalisation), in fp64.
+    // weights in fp64: renormalised, the softmax restricted to the selected
+    // experts (the full softmax denominator cancels); else the softmax over
+    // all E experts at the selected ones
     const double ex = (lane < k) ? exp((double)mine - (double)first) : 0.0;
-    const double s = wave_sum_f64(ex);
+    const double s = wave_sum_f64(renorm ? ex : (lane < E ? exp((double)lg[r][lane] - (double)first) : 0.0));
     if (lane < k) topw[(size_t)t * k + lane] = (float)(ex / s);
   }
   if (hist != nullptr) {
@@ -194,10 +196,11 @@ hipError_t launch_route(const Shape& s, const void* x, const float* wg, const fl
   const dim3 block(kRouteWaves * 64);
   if (s.bf16)
     hipLaunchKernelGGL(route_kernel<uint16_t>, dim3(blocks), block, 0, st,
-                       (const uint16_t*)x, wg, bias, s.T, s.H, s.E, s.k, logits, ids, w, hist);
+                       (const uint16_t*)x, wg, bias, s.T, s.H, s.E, s.k, logits, ids, w, hist,
+                       (int)s.renorm);
   else
     hipLaunchKernelGGL(route_kernel<float>, dim3(blocks), block, 0, st, (const float*)x, wg,
-                       bias, s.T, s.H, s.E, s.k, logits, ids, w, hist);
+                       bias, s.T, s.H, s.E, s.k, logits, ids, w, hist, (int)s.renorm);
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ def device_inputs(inp: mi.LayerInputs, device="cuda") -> dict:
 
 def shape_of(sp: mi.LayerSpec):
     from mixture_experts_ffn_moe_amd import make_shape
-    return make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
+    return make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype, sp.renormalize)
 
 
 def out_dtype(sp):

@@ -144,6 +144,30 @@ def test_zero_tokens_is_a_no_op(m):
     assert lib.moe_grouped_gemm_w13_swiglu(ctypes.byref(s), P, P, P, P, P, None) == m.MOE_OK
 
 
+def test_renormalize_flag(m):
+    """renormalize is 0 or 1; anything else is an invalid argument."""
+    lib = m._lib.lib
+    P = ctypes.c_void_p(4096)
+    for v, want in ((0, m.MOE_OK), (1, m.MOE_OK), (2, m.MOE_ERR_INVALID_ARG), (-1, m.MOE_ERR_INVALID_ARG)):
+        s = m.make_shape(64, 256, 8, 2, 128, 1, "bf16")
+        s.renormalize = v
+        assert (lib.moe_workspace_size(ctypes.byref(s)) > 0) == (want == m.MOE_OK)
+        if want != m.MOE_OK:
+            assert lib.moe_route(ctypes.byref(s), P, P, None, P, P, P, None) == want
+    assert m.make_shape(64, 256, 8, 2, 128, 1, "bf16").renormalize == 1
+    assert m.make_shape(64, 256, 8, 2, 128, 1, "bf16", renormalize=False).renormalize == 0
+
+
+def test_shape_struct_matches_header(m):
+    """The ctypes mirror of moe_shape has the header's fields, in order."""
+    import re
+    hdr = open(os.path.join(ROOT, "include", "moe_mi355x.h")).read()
+    body = re.search(r"typedef struct \{(.*?)\} moe_shape;", hdr, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [f[0] for f in m.MoeShape._fields_]
+
+
 def test_binding_raises_on_error(m):
     s = m.make_shape(64, 256, 65, 2, 128, 1, "bf16")
     with pytest.raises(m.MoeError) as ei:

@@ -1,0 +1,90 @@
+"""Source rules of the HIP kernels, checked on the CPU.
+
+An inline-asm memory load whose destination is a vector register is
+invisible to the compiler's wait-count tracking: the compiler takes the
+asm's output as written when the asm issues, and may copy or reuse that
+register while the load is still in flight, so data landing late
+overwrites a live value (an address, say) and the GPU faults.  The
+library's asm loads write LDS only (direct-to-LDS copies) and have no
+register outputs; loads into registers are written as ordinary C++ loads,
+which the compiler tracks.  This test keeps it that way, and checks that
+an asm statement that sets m0 (the LDS address of a direct-to-LDS copy)
+names m0 as clobbered.
+"""
+import glob
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixture_experts_ffn_moe_amd", "csrc")
+
+_ASM = re.compile(r"\basm\s*(?:volatile\s*|__volatile__\s*)?\(", re.S)
+_STR = re.compile(r'\s*"((?:[^"\\]|\\.)*)"', re.S)
+
+
+def asm_blocks(src):
+    """(template, outputs) of every inline-asm statement in src."""
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = []
+    for m in _ASM.finditer(src):
+        i = m.end()
+        parts = []
+        while True:
+            s = _STR.match(src, i)
+            if not s:
+                break
+            parts.append(s.group(1))
+            i = s.end()
+        # operand sections up to the closing parenthesis of the statement
+        depth, j = 1, i
+        while depth and j < len(src):
+            depth += {"(": 1, ")": -1}.get(src[j], 0)
+            j += 1
+        rest = src[i:j - 1]
+        sections = rest.lstrip()[1:].split(":") if rest.lstrip().startswith(":") else []
+        outputs = sections[0] if sections else ""
+        clobbers = sections[2] if len(sections) > 2 else ""
+        out.append(("".join(parts), outputs, clobbers))
+    return out
+
+
+def register_output_loads(src):
+    bad = []
+    for tmpl, outputs, _ in asm_blocks(src):
+        is_load = re.search(r"\b(global|buffer|flat|scratch)_load\w*|\bds_read\w*", tmpl)
+        # an output operand in a vector or accumulation register
+        reg_out = re.search(r'"[=+]&?[va]"', outputs)
+        direct_to_lds = re.search(r"_load_lds_", tmpl)
+        if is_load and reg_out and not direct_to_lds:
+            bad.append(tmpl)
+    return bad
+
+
+def m0_unclobbered(src):
+    """asm statements that write m0 without naming it as clobbered (the
+    compiler could otherwise keep a live value of its own in m0)."""
+    return [t for t, _, clob in asm_blocks(src)
+            if re.search(r"\bs_mov_b32\s+m0\b", t) and '"m0"' not in clob]
+
+
+def test_rule_detects_a_register_output_load():
+    planted = 'asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");'
+    assert register_output_loads(planted)
+    clean = 'asm volatile("s_mov_b32 m0, %0\\n\\tglobal_load_lds_dwordx4 %1, %2" :: "s"(a), "v"(o), "s"(b) : "memory", "m0");'
+    assert not register_output_loads(clean)
+    assert len(asm_blocks(clean)) == 1
+    assert not m0_unclobbered(clean)
+    assert m0_unclobbered(clean.replace(', "m0"', ""))
+
+
+def test_no_inline_asm_load_into_registers():
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+    assert files
+    n = 0
+    for f in files:
+        src = open(f).read()
+        n += len(asm_blocks(src))
+        assert not register_output_loads(src), f"{os.path.basename(f)}: inline-asm load into a register"
+        assert not m0_unclobbered(src), f"{os.path.basename(f)}: asm writes m0 without clobbering it"
+    assert n >= 1  # the direct-to-LDS copy is asm
