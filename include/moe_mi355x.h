@@ -179,6 +179,27 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, c
                        const void* w1, const void* w2, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same layer and launch sequence as moe_forward, with the workspace
+ * taken from a static device array of MOE_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds on each GPU it runs on until the process ends (set up on
+ * the first call on a device, which must be the current device; no
+ * hipMalloc, hipFree or other allocation, ever).  Inputs and output are the
+ * caller's, as for moe_forward.
+ *   Shapes whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES (the
+ *   small-token regime fits: the decode layer T=8, H=4096, E=64, k=8, Im=768
+ *   needs under 1 MiB) are rejected with MOE_ERR_WORKSPACE before anything is
+ *   enqueued.
+ *   Every call on one GPU uses that GPU's one array and leaves the call's
+ *   intermediates in it: calls that may overlap on one GPU (other streams,
+ *   other threads) race and must be serialised by the caller.  No kernel of
+ *   the call needs the array cleared beforehand. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* wg,
+                               const float* bias, const void* w1, const void* w2, void* out,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTED = (
     "moe_status_string", "moe_workspace_size", "moe_get_workspace_layout", "moe_route",
     "moe_permute", "moe_grouped_gemm_w13_swiglu", "moe_grouped_gemm_down", "moe_finalize",
-    "moe_forward",
+    "moe_forward", "moe_forward_noalloc",
     # shared expert (moe_shared.h)
     "moe_shared_workspace_size", "moe_get_shared_workspace_layout", "moe_shared_ffn",
     "moe_finalize_shared", "moe_forward_shared",
@@ -79,6 +79,8 @@ def _load():
     lib.moe_finalize.restype = i32
     lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_forward.restype = i32
+    lib.moe_forward_noalloc.argtypes = [S, P, P, P, P, P, P, P]
+    lib.moe_forward_noalloc.restype = i32
     lib.moe_shared_workspace_size.argtypes = [S, i32]
     lib.moe_shared_workspace_size.restype = ctypes.c_size_t
     lib.moe_get_shared_workspace_layout.argtypes = [S, i32, ctypes.POINTER(MoeSharedLayout)]
@@ -232,6 +234,22 @@ def moe_forward(shape, x, wg, bias, w1, w2, out, workspace, stream=None):
                            _arg("w1", w1, dt, mu * E * 2 * Im * H), _arg("w2", w2, dt, mu * E * H * Im),
                            _arg("out", out, dt, T * H), ws, nbytes, _stream(stream)),
            "moe_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MOE_NOALLOC_SCRATCH_BYTES of moe_mi355x.h
+
+
+def moe_forward_noalloc(shape, x, wg, bias, w1, w2, out, stream=None):
+    """moe_forward on the library's static per-GPU scratch (no workspace)."""
+    T, H, E, Im, mu = shape.T, shape.H, shape.E, shape.Im, shape.micro_count
+    dt = _layer_dtype(shape)
+    _check(lib.moe_forward_noalloc(ctypes.byref(shape), _arg("x", x, dt, T * H),
+                                   _arg("wg", wg, torch.float32, E * H),
+                                   _arg("gate_bias", bias, torch.float32, E, nullable=True),
+                                   _arg("w1", w1, dt, mu * E * 2 * Im * H),
+                                   _arg("w2", w2, dt, mu * E * H * Im),
+                                   _arg("out", out, dt, T * H), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_shared_workspace_size(shape: MoeShape, Is: int) -> int:

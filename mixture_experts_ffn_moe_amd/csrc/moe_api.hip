@@ -9,8 +9,14 @@
 #include "moe_common.h"
 
 #include <algorithm>
+#include <mutex>
 
 using moe::Shape;
+
+// Scratch of moe_forward_noalloc: one copy per GPU, held until the process
+// ends.  In host code this name is only a stand-in for the symbol; the device
+// address of each GPU's copy comes from hipGetSymbolAddress (noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -177,6 +183,26 @@ moe_status forward_impl(const Shape& s, const void* x, const float* wg, const fl
   return MOE_OK;
 }
 
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -278,6 +304,26 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, c
   if (bias != nullptr) MOE_CHECK(check_ptr(bias));
   return forward_impl(s, x, wg, bias, w1, w2, out, workspace, workspace_bytes, (hipStream_t)stream,
                       nullptr);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* wg,
+                               const float* bias, const void* w1, const void* w2, void* out,
+                               void* stream) {
+  Shape s;
+  MOE_CHECK(check_shape(shape, &s));
+  if (s.T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x)); MOE_CHECK(check_ptr(wg)); MOE_CHECK(check_ptr(w1));
+  MOE_CHECK(check_ptr(w2)); MOE_CHECK(check_ptr(out));
+  if (bias != nullptr) MOE_CHECK(check_ptr(bias));
+  moe_workspace_layout L;
+  layout_of(s, &L);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  MOE_CHECK(noalloc_scratch(&ws));
+  // the same launch sequence as moe_forward, on the device's static scratch
+  // (no kernel of it needs the workspace cleared first)
+  return forward_impl(s, x, wg, bias, w1, w2, out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES,
+                      (hipStream_t)stream, nullptr);
 }
 
 // ---- shared expert (moe_shared.h)
