@@ -236,7 +236,8 @@ def time_kernels(moe, torch, d, steps, warmup):
     L, ids, w = f(T, E), f(T, k, dtype=torch.int32), f(T, k)
     cnt, off = f(E, dtype=torch.int32), f(E + 1, dtype=torch.int32)
     perm, inv = f(R, dtype=torch.int32), f(R, dtype=torch.int32)
-    h, y, out = f(R, sp.I, dtype=dt), f(R, H, dtype=dt), f(T, H, dtype=dt)
+    h, out = f(R, sp.I, dtype=dt), f(T, H, dtype=dt)
+    y = f(moe.y_nbytes(s, R), dtype=torch.uint8)  # block-scaled half (fp32 in the fp32 layer)
     names = ["route", "permute", "w13_swiglu", "down", "finalize"]
     calls = [
         lambda: moe.moe_route(s, d["x"], d["wg"], d["bias"], L, ids, w),

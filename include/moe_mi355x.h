@@ -29,8 +29,19 @@
  *
  * Notation: T tokens, H hidden size, E experts, k routes per token,
  * Im intermediate columns per micro-shard, mu = micro_count, R = T*k routes.
- * dtype is the element type of x, w1, w2, h, y and out (MOE_BF16 or
- * MOE_F32); router weights, bias, logits and routing weights are always fp32.
+ * dtype is the element type of x, w1, w2, h and out (MOE_BF16 or MOE_F32);
+ * router weights, bias, logits and routing weights are always fp32.
+ *
+ * y, the down projection's output [rows, H] that the finalize consumes, is
+ * fp32 in an MOE_F32 layer.  In an MOE_BF16 layer it is "block-scaled half":
+ * each row is cut into blocks of MOE_Y_BLOCK columns; the buffer holds the
+ * values as fp16 [rows, H] followed by one int8 exponent per block
+ * [rows, H / MOE_Y_BLOCK], and y[p, n] = value[p, n] * 2^exponent[p, n / MOE_Y_BLOCK].
+ * A block's exponent is floor(log2 M) - 14 for its largest magnitude M (0 for
+ * an all-zero block), so every value keeps 11 significant bits in the bytes of
+ * bf16 plus one per block.  (A bf16 y would be a third rounding between the
+ * fp32 accumulator and the output; at outputs of magnitude 4 and more that
+ * takes the error past the bf16 bar of 2e-2.)  Size: MOE_Y_BYTES(dtype, rows, H).
  *
  * Envelope (MOE_ERR_UNSUPPORTED outside it): 1 <= E <= 64, H % 256 == 0,
  * Im % 128 == 0, R < 2^31, every size in elements < 2^31, one expert's w1
@@ -56,6 +67,12 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Columns per exponent of a block-scaled half y, and the bytes of a y buffer. */
+#define MOE_Y_BLOCK 256
+#define MOE_Y_BYTES(dtype, rows, H)                                                        \
+  ((dtype) == MOE_BF16 ? (size_t)(rows) * (size_t)(H) * 2 + (size_t)(rows) * ((H) / MOE_Y_BLOCK) \
+                       : (size_t)(rows) * (size_t)(H) * 4)
+
 typedef struct {
   int32_t T;            /* tokens, >= 0 */
   int32_t H;            /* hidden size */
@@ -79,7 +96,7 @@ typedef struct {
   size_t perm;     /* int32   [R]            */
   size_t inv;      /* int32   [R]            */
   size_t h;        /* dtype   [R, mu*Im]     */
-  size_t y;        /* dtype   [R, H]         */
+  size_t y;        /* y       [R, H] (fp32, or block-scaled half for bf16) */
   size_t scratch;  /* token path: int32 [ceil(T/16), 64] expert counts per 16-token router
                       block; small-token path: fp64 router partials, active-expert list */
   size_t total;    /* bytes needed            */
@@ -146,17 +163,19 @@ moe_status moe_grouped_gemm_w13_swiglu(const moe_shape* shape, const void* x, co
 /* Grouped down GEMM with micro-shards summed in the accumulator (hybrid
  * parallelism, section 6.1: grouped GEMM2 per micro, partials added in fp32).
  *   w2 [mu, E, H, Im] dtype, micro-major.
- *   y[p, n] = sum_m sum_i h[p, m*Im + i] * w2[m][e][n][i], fp32 accumulation,
- *   one rounding to dtype.  Output y [R, H] dtype.  offsets as for the w13
- *   GEMM (moe_permute's, used unchecked). */
+ *   y[p, n] = sum_m sum_i h[p, m*Im + i] * w2[m][e][n][i], fp32 accumulation.
+ *   Output y [R, H]: fp32 (MOE_F32), block-scaled half (MOE_BF16; see above),
+ *   MOE_Y_BYTES(dtype, R, H) bytes.  offsets as for the w13 GEMM
+ *   (moe_permute's, used unchecked). */
 moe_status moe_grouped_gemm_down(const moe_shape* shape, const void* h, const int32_t* offsets,
                                  const void* w2, void* y, void* stream);
 
 /* Finalize: routing scale and top-k reduction once (hybrid parallelism,
  * section 6.1, the finalize formula).
  *   out[t, :] = sum_{j = 0..k-1} topk_w[t, j] * y[inv[t*k + j], :], fp32,
- *   j ascending, one rounding to dtype.  Output out [T, H] dtype.  inv must
- *   be moe_permute's (values in [0, R), used unchecked). */
+ *   j ascending, one rounding to dtype.  y [R, H] as moe_grouped_gemm_down
+ *   writes it.  Output out [T, H] dtype.  inv must be moe_permute's (values in
+ *   [0, R), used unchecked). */
 moe_status moe_finalize(const moe_shape* shape, const void* y, const int32_t* inv,
                         const float* topk_w, void* out, void* stream);
 
@@ -172,9 +191,11 @@ moe_status moe_finalize(const moe_shape* shape, const void* y, const int32_t* in
  *   weight-streaming path (the AR-decode regime: hybrid parallelism,
  *   sections 4.3 and 6.2): routing, counts, offsets, perm and inv are the
  *   same bits as the step-wise path, h is computed the same way, and the down
- *   projection is fused with the finalize (no rounding of y to dtype), so the
- *   output matches the step-wise path within rounding, not bit for bit; the
- *   y region is then left untouched.  Output out [T, H] dtype. */
+ *   projection is fused with the finalize (y is never written; its fp32 values
+ *   are summed unrounded and in another order), so the output matches the
+ *   step-wise path within rounding, not bit for bit; the y region is then
+ *   left untouched.
+ *   Output out [T, H] dtype. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* wg, const float* bias,
                        const void* w1, const void* w2, void* out,
                        void* workspace, size_t workspace_bytes, void* stream);

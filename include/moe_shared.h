@@ -24,8 +24,10 @@
  * enqueued and no output is touched; T == 0 is valid and enqueues nothing.
  *
  * Layouts: w1s [2*Is, H] dtype, rows [0, Is) gate and [Is, 2*Is) the
- * matching up rows; w2s [H, Is] dtype; hs [T, Is] dtype; ys [T, H] dtype.
- * Sums are in fp32 and every dtype result is rounded once.
+ * matching up rows; w2s [H, Is] dtype; hs [T, Is] dtype; ys [T, H] in the
+ * format of the routed y (moe_mi355x.h: fp32, or block-scaled half in a bf16
+ * layer; MOE_Y_BYTES(dtype, T, H) bytes).  Sums are in fp32 and every dtype
+ * result is rounded once.
  *
  * Envelope, beside moe_mi355x.h's: Is % 128 == 0, T*Is < 2^31, the w1s block
  * (2*Is*H elements of 2 bytes) < 4 GiB; otherwise MOE_ERR_UNSUPPORTED.
@@ -46,7 +48,7 @@ extern "C" {
  * the shared regions follow it, each 256-byte aligned. */
 typedef struct {
   size_t hs;     /* dtype [T, Is]: the shared expert's SwiGLU activations */
-  size_t ys;     /* dtype [T, H]: its output (token path only; the small-token
+  size_t ys;     /* y format [T, H]: its output (token path only; the small-token
                     path fuses it into the output and leaves this region alone) */
   size_t total;  /* bytes needed */
 } moe_shared_layout;
@@ -63,13 +65,13 @@ moe_status moe_get_shared_workspace_layout(const moe_shape* shape, int32_t Is,
  * down GEMMs of moe_mi355x.h run on one dense segment of the T tokens in
  * order.
  *   x [T, H], w1s [2*Is, H], w2s [H, Is] (dtype).
- * Outputs: hs [T, Is] and ys [T, H] (dtype). */
+ * Outputs: hs [T, Is] (dtype) and ys [T, H] (y format). */
 moe_status moe_shared_ffn(const moe_shape* shape, int32_t Is, const void* x, const void* w1s,
                           const void* w2s, void* hs, void* ys, void* stream);
 
 /* moe_finalize plus the shared expert's output: the routed sum over j
  * ascending in fp32, then + ys[t, :], one rounding.
- *   y [R, H] dtype, inv [R] int32, topk_w [T, k] fp32, ys [T, H] dtype.
+ *   y [R, H] and ys [T, H] (y format), inv [R] int32, topk_w [T, k] fp32.
  * Output: out [T, H] dtype. */
 moe_status moe_finalize_shared(const moe_shape* shape, const void* y, const int32_t* inv,
                                const float* topk_w, const void* ys, void* out, void* stream);

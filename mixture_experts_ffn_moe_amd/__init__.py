@@ -13,6 +13,6 @@ from ._lib import (  # noqa: F401
     moe_finalize_shared, moe_forward, moe_forward_noalloc, moe_forward_shared, moe_get_shared_workspace_layout,
     moe_get_workspace_layout, moe_grouped_gemm_down, moe_grouped_gemm_w13_swiglu, moe_permute,
     moe_probe_mfma_bf16, moe_probe_read, moe_route, moe_shared_ffn, moe_shared_workspace_size,
-    moe_workspace_size, status_string,
+    moe_workspace_size, status_string, y_nbytes,
 )
 from .layer import MoELayerBuffers, workspace_views  # noqa: F401

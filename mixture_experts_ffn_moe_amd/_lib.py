@@ -143,6 +143,32 @@ def _arg(name: str, t, dtype: torch.dtype, numel: int, nullable: bool = False):
     return _ptr(t)
 
 
+Y_BLOCK = 256  # columns per exponent of a block-scaled half y (moe_mi355x.h)
+
+
+def y_nbytes(shape, rows: int) -> int:
+    """Bytes of a y buffer of `rows` rows: block-scaled half (fp16 values,
+    then one int8 exponent per Y_BLOCK columns) in the bf16 layers, fp32 in
+    the fp32 layer."""
+    H = shape.H
+    if shape.dtype == MOE_BF16:
+        return rows * H * 2 + rows * (H // Y_BLOCK)
+    return rows * H * 4
+
+
+def _arg_bytes(name: str, t, nbytes: int):
+    """A contiguous GPU tensor of exactly nbytes bytes (any element type)."""
+    if t is None:
+        raise ValueError(f"{name}: a tensor is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
+    if t.numel() * t.element_size() != nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, expected {nbytes} for this shape")
+    return _ptr(t)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -204,7 +230,7 @@ def moe_grouped_gemm_down(shape, h, offsets, w2, y, stream=None):
     dt = _layer_dtype(shape)
     _check(lib.moe_grouped_gemm_down(ctypes.byref(shape), _arg("h", h, dt, R * mu * Im),
                                      _arg("offsets", offsets, torch.int32, E + 1),
-                                     _arg("w2", w2, dt, mu * E * H * Im), _arg("y", y, dt, R * H),
+                                     _arg("w2", w2, dt, mu * E * H * Im), _arg_bytes("y", y, y_nbytes(shape, R)),
                                      _stream(stream)), "moe_grouped_gemm_down")
 
 
@@ -212,7 +238,8 @@ def moe_finalize(shape, y, inv, topk_w, out, stream=None):
     T, H, k = shape.T, shape.H, shape.k
     R = T * k
     dt = _layer_dtype(shape)
-    _check(lib.moe_finalize(ctypes.byref(shape), _arg("y", y, dt, R * H), _arg("inv", inv, torch.int32, R),
+    _check(lib.moe_finalize(ctypes.byref(shape), _arg_bytes("y", y, y_nbytes(shape, R)),
+                            _arg("inv", inv, torch.int32, R),
                             _arg("topk_w", topk_w, torch.float32, R), _arg("out", out, dt, T * H),
                             _stream(stream)), "moe_finalize")
 
@@ -268,7 +295,8 @@ def moe_shared_ffn(shape, Is, x, w1s, w2s, hs, ys, stream=None):
     dt = _layer_dtype(shape)
     _check(lib.moe_shared_ffn(ctypes.byref(shape), int(Is), _arg("x", x, dt, T * H),
                               _arg("w1s", w1s, dt, 2 * Is * H), _arg("w2s", w2s, dt, H * Is),
-                              _arg("hs", hs, dt, T * Is), _arg("ys", ys, dt, T * H), _stream(stream)),
+                              _arg("hs", hs, dt, T * Is), _arg_bytes("ys", ys, y_nbytes(shape, T)),
+                              _stream(stream)),
            "moe_shared_ffn")
 
 
@@ -276,8 +304,9 @@ def moe_finalize_shared(shape, y, inv, topk_w, ys, out, stream=None):
     T, H, k = shape.T, shape.H, shape.k
     R = T * k
     dt = _layer_dtype(shape)
-    _check(lib.moe_finalize_shared(ctypes.byref(shape), _arg("y", y, dt, R * H), _arg("inv", inv, torch.int32, R),
-                                   _arg("topk_w", topk_w, torch.float32, R), _arg("ys", ys, dt, T * H),
+    _check(lib.moe_finalize_shared(ctypes.byref(shape), _arg_bytes("y", y, y_nbytes(shape, R)),
+                                   _arg("inv", inv, torch.int32, R),
+                                   _arg("topk_w", topk_w, torch.float32, R), _arg_bytes("ys", ys, y_nbytes(shape, T)),
                                    _arg("out", out, dt, T * H), _stream(stream)), "moe_finalize_shared")
 
 

@@ -4,7 +4,8 @@
 // expert outputs by original token and top-k slot through the inverse
 // permutation, applies the routing score once and reduces the top-k routes
 // once.  The micro-shard partials were already summed in the down GEMM's fp32
-// accumulator, so each route contributes one row of y.
+// accumulator, so each route contributes one row of y: fp32 in the fp32 layer,
+// block-scaled half (11 significant bits, moe_common.h) in the bf16 layers.
 //
 // out[t, :] = sum_{j ascending} w[t, j] * y[inv[t*k + j], :] in fp32, one
 // rounding.  With a shared expert ("HunyuanImage-3.0 on CANN NPU", section
@@ -18,13 +19,37 @@
 namespace moe {
 namespace {
 
-template <typename T>
-__global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ y,
+// One route row's 8 columns [c, c + 8) as fp32: fp32 y (the fp32 layer) or
+// block-scaled half y (the bf16 layers; values plane `y`, exponents `ye`).
+struct YRow {
+  __device__ __forceinline__ static void load(const float* y, const int8_t*, size_t row, int H, int c,
+                                              float (&v)[8]) {
+    const float4* src = reinterpret_cast<const float4*>(y + row * H + c);
+    const float4 a = src[0], b = src[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void load(const _Float16* y, const int8_t* ye, size_t row, int H, int c,
+                                              float (&v)[8]) {
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    const f16x8 h = *reinterpret_cast<const f16x8*>(y + row * H + c);
+    const int e = ye[row * (H / kYBlock) + c / kYBlock];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = ldexpf((float)h[q], e);
+  }
+};
+
+// out has the layer's element type T; y and ys are fp32 for the fp32 layer
+// and block-scaled half (values YT = _Float16 plus int8 exponents) for the
+// bf16 layers.  A thread owns 8 consecutive columns (within one y block).
+template <typename T, typename YT>
+__global__ __launch_bounds__(256) void finalize_kernel(const YT* __restrict__ y,
+                                                       const int8_t* __restrict__ ye,
                                                        const int32_t* __restrict__ inv,
                                                        const float* __restrict__ w,
-                                                       const T* __restrict__ ys, int H, int k,
+                                                       const YT* __restrict__ ys,
+                                                       const int8_t* __restrict__ yse, int H, int k,
                                                        T* __restrict__ out) {
-  constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int V = 8;  // columns per thread
   const int t = blockIdx.x;
   const int32_t* rows = inv + (size_t)t * k;
   const float* wt = w + (size_t)t * k;
@@ -32,40 +57,39 @@ __global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ y,
     float acc[V];
 #pragma unroll
     for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-    // routes in groups of 8: a group's row loads are all in flight before the
-    // first is used (7% faster than one at a time); the sum still runs over j
-    // ascending
+    // routes in groups of 4: a group's row loads are all in flight before the
+    // first is used; the sum still runs over j ascending
     int j = 0;
-    for (; j + 8 <= k; j += 8) {
-      uint4 raw[8];
+    for (; j + 4 <= k; j += 4) {
+      float v[4][V];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) raw[u] = *reinterpret_cast<const uint4*>(y + (size_t)rows[j + u] * H + c);
+      for (int u = 0; u < 4; ++u) YRow::load(y, ye, (size_t)rows[j + u], H, c, v[u]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 4; ++u) {
         const float s = wt[j + u];
-        const T* v = reinterpret_cast<const T*>(&raw[u]);
 #pragma unroll
-        for (int q = 0; q < V; ++q) acc[q] = fmaf(s, Elem<T>::to_f(v[q]), acc[q]);
+        for (int q = 0; q < V; ++q) acc[q] = fmaf(s, v[u][q], acc[q]);
       }
     }
     for (; j < k; ++j) {
+      float v[V];
+      YRow::load(y, ye, (size_t)rows[j], H, c, v);
       const float s = wt[j];
-      const uint4 raw = *reinterpret_cast<const uint4*>(y + (size_t)rows[j] * H + c);
-      const T* v = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] = fmaf(s, Elem<T>::to_f(v[q]), acc[q]);
+      for (int q = 0; q < V; ++q) acc[q] = fmaf(s, v[q], acc[q]);
     }
     if (ys != nullptr) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(ys + (size_t)t * H + c);
-      const T* v = reinterpret_cast<const T*>(&raw);
+      float v[V];
+      YRow::load(ys, yse, (size_t)t, H, c, v);
 #pragma unroll
-      for (int q = 0; q < V; ++q) acc[q] += Elem<T>::to_f(v[q]);
+      for (int q = 0; q < V; ++q) acc[q] += v[q];
     }
-    uint4 res;
-    T* o = reinterpret_cast<T*>(&res);
+    alignas(16) T res[V];
 #pragma unroll
-    for (int q = 0; q < V; ++q) o[q] = Elem<T>::from_f(acc[q]);
-    *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = res;
+    for (int q = 0; q < V; ++q) res[q] = Elem<T>::from_f(acc[q]);
+    uint4* dst = reinterpret_cast<uint4*>(out + (size_t)t * H + c);
+#pragma unroll
+    for (int q = 0; q < V * (int)sizeof(T) / 16; ++q) dst[q] = reinterpret_cast<const uint4*>(res)[q];
   }
 }
 
@@ -73,12 +97,18 @@ __global__ __launch_bounds__(256) void finalize_kernel(const T* __restrict__ y,
 
 hipError_t launch_finalize(const Shape& s, const void* y, const int32_t* inv, const float* w,
                            void* out, hipStream_t st, const void* ys) {
-  if (s.bf16)
-    hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3(s.T), dim3(256), 0, st,
-                       (const uint16_t*)y, inv, w, (const uint16_t*)ys, s.H, s.k, (uint16_t*)out);
-  else
-    hipLaunchKernelGGL(finalize_kernel<float>, dim3(s.T), dim3(256), 0, st, (const float*)y, inv,
-                       w, (const float*)ys, s.H, s.k, (float*)out);
+  if (s.bf16) {
+    // block-scaled half: the exponent plane follows the values plane
+    const int8_t* ye = (const int8_t*)y + (size_t)s.R() * s.H * 2;
+    const int8_t* yse = ys ? (const int8_t*)ys + (size_t)s.T * s.H * 2 : nullptr;
+    hipLaunchKernelGGL((finalize_kernel<uint16_t, _Float16>), dim3(s.T), dim3(256), 0, st,
+                       (const _Float16*)y, ye, inv, w, (const _Float16*)ys, yse, s.H, s.k,
+                       (uint16_t*)out);
+  } else {
+    hipLaunchKernelGGL((finalize_kernel<float, float>), dim3(s.T), dim3(256), 0, st, (const float*)y,
+                       (const int8_t*)nullptr, inv, w, (const float*)ys, (const int8_t*)nullptr, s.H,
+                       s.k, (float*)out);
+  }
   return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@
 //     applied in registers before the single rounding of h.
 //   * down mode: the K loop runs over all micros' intermediate columns; the B
 //     pointer switches micro at each Im boundary, so the per-micro partials
-//     are summed in the fp32 accumulator and never exist as tensors.
+//     are summed in the fp32 accumulator and never exist as tensors; y
+//     leaves as that fp32 accumulator (no rounding before the finalize).
 //
 // Work decomposition: a logical tile is (expert e, n-tile, m-tile of BM rows
 // of e's segment), numbered expert-major, then n-tile, then m-tile, so
@@ -178,14 +179,14 @@ hipError_t launch_w13_swiglu(const Shape& s, const void* x, const int32_t* perm,
 hipError_t launch_w13_swiglu_with_dense(const Shape& s, const void* x, const int32_t* perm,
                                         const int32_t* offsets, const void* w1, void* h,
                                         const void* w1d, void* hd, int wd, hipStream_t st) {
-  const fast::Extra ex{(const uint16_t*)x, (const uint16_t*)w1d, (uint16_t*)hd, s.T, wd};
+  const fast::Extra ex{(const uint16_t*)x, (const uint16_t*)w1d, hd, s.T, wd};
   return fast::launch<W13Cfg>(x, perm, offsets, w1, h, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
 }
 
 hipError_t launch_down_with_dense(const Shape& s, const void* h, const int32_t* offsets,
                                   const void* w2, void* y, const void* hd, const void* w2d,
                                   void* yd, int wd, hipStream_t st) {
-  const fast::Extra ex{(const uint16_t*)hd, (const uint16_t*)w2d, (uint16_t*)yd, s.T, wd};
+  const fast::Extra ex{(const uint16_t*)hd, (const uint16_t*)w2d, yd, s.T, wd};
   return fast::launch<DownCfg>(h, nullptr, offsets, w2, y, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
 }
 

@@ -48,6 +48,9 @@ struct Cfg {
   static constexpr int STAGE = (BM + BN) * BK;        // bf16 elements per stage
   static constexpr int LDS_BYTES = (STAGES * BM + SB * BN) * BK * 2;
   static constexpr int HCOLS = (MODE == kW13) ? BN / 2 : BN;  // output columns per tile
+  // h leaves the w13 GEMM rounded to bf16 (the down GEMM's MFMA operand); y
+  // leaves block-scaled half, one block of kYBlock columns per tile row
+  static_assert(MODE == kW13 || BN == kYBlock, "one y block per tile row");
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "load split");
   static_assert(TM % 16 == 0 && TN % 32 == 0, "wave tile");
@@ -101,7 +104,7 @@ struct Tile {
 struct Extra {
   const uint16_t* a;
   const uint16_t* b;
-  uint16_t* c;
+  void* c;  // bf16 in w13 mode, block-scaled half of `rows` rows in down mode
   int rows, w;
 };
 
@@ -227,7 +230,7 @@ __device__ __forceinline__ Tile decode_wave(const int32_t* __restrict__ offsets,
 template <class C, bool PART = true, bool EQ = true, bool XS = false>
 __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B, uint16_t* __restrict__ Cout,
+    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B, void* __restrict__ Cout,
     int H, int E, int k, int Im, int mu, int n_tiles, int dense_rows, Extra ex) {
   // A ring (STAGES slots of BM x BK) followed by the B ring (SB slots of BN x BK)
   __shared__ __attribute__((aligned(1024))) uint16_t smem[(C::STAGES * C::BM + C::SB * C::BN) * C::BK];
@@ -460,19 +463,65 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
   // passed the barrier) and leaves as whole 128-byte lines, 16 bytes per lane
   // (the down GEMM, whose tiles are short in K, ran 8% faster so).
   constexpr int OC = (C::MODE == kW13) ? C::HCOLS : C::BN;  // output columns of the tile
-  constexpr int OS = OC * 2 + 16;  // LDS row stride in bytes: rows 4 banks apart
+  constexpr int OB = 2;             // bf16 h, or the fp16 values of y
+  constexpr int OS = OC * OB + 16;  // LDS row stride in bytes: rows 4 banks apart
   // the whole tile in one pass when it fits the ring, else one wave-row block
   // (TM rows) per pass
   constexpr int PASSES = (C::BM * OS <= C::LDS_BYTES) ? 1 : C::WM;
   constexpr int PROWS = C::BM / PASSES;
   static_assert(PROWS * OS <= C::LDS_BYTES, "output rows of a pass fit the ring");
-  constexpr int LPR = OC * 2 / 16, RPW = kWave / LPR;  // lanes per row, rows per store
+  constexpr int LPR = OC * OB / 16, RPW = kWave / LPR;  // lanes per row, rows per store
+  static_assert(LPR <= kWave && kWave % LPR == 0, "store lanes");
   const int ldc = (C::MODE == kW13) ? mu * Im : H;
   const int cq = 4 * (lane >> 4);
   const int rows = ti.seg_end - ti.m0;
   const int col0 = (C::MODE == kW13) ? micro * Im + n0 : n0;
   const int cb = (lane % LPR) * 16;
   char* so = reinterpret_cast<char*>(smem);
+
+  // y (down): block-scaled half, one block = the tile row's BN columns.  A
+  // row's block maximum: over the lane's values, across the four lanes that
+  // share the row (lane ^ 16, lane ^ 32), then across the two waves that hold
+  // its column halves (through LDS, past the staging area); the accumulators
+  // are then scaled by 2^-e in registers and staged as fp16.
+  if constexpr (C::MODE == kDown) {
+    static_assert(C::WN == 2 && C::TN * 2 == C::BN, "two waves share a tile row");
+    constexpr int MAX_OFF = C::LDS_BYTES - 2 * C::BM * 4;
+    static_assert(MAX_OFF >= PROWS * OS, "row maxima past the staging rows");
+    float* smax = reinterpret_cast<float*>(so + MAX_OFF);
+    float rmax[C::FM];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(acc[i][j][r]));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      rmax[i] = m;
+    }
+    __syncthreads();  // every wave is past its last k-step: the ring is free
+    if (lane < 16) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) smax[wn * C::BM + wm * C::TM + 16 * i + lane] = rmax[i];
+    }
+    __syncthreads();
+    const size_t out_rows = xt ? (size_t)ex.rows : (size_t)dense_rows * (size_t)k;
+    int8_t* ye = reinterpret_cast<int8_t*>(reinterpret_cast<char*>(Cout) + out_rows * (size_t)ldc * 2);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int tr = wm * C::TM + 16 * i + (lane & 15);  // tile row
+      const int e = yexp_of(fmaxf(rmax[i], smax[(1 - wn) * C::BM + tr]));
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = ldexpf(acc[i][j][r], -e);
+      if (wn == 0 && lane < 16 && tr < rows)
+        ye[(size_t)(ti.m0 + tr) * (size_t)(ldc / kYBlock) + col0 / kYBlock] = (int8_t)e;
+    }
+  }
+
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
     __syncthreads();
@@ -489,9 +538,14 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
             *reinterpret_cast<uint2*>(so + rt * OS + (wn * (C::TN / 2) + 16 * j + cq) * 2) = pack_bf16x4(v);
           }
         } else {
+          typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            *reinterpret_cast<uint2*>(so + rt * OS + (wn * C::TN + 16 * j + cq) * 2) = pack_bf16x4(acc[i][j]);
+          for (int j = 0; j < C::FN; ++j) {
+            f16x4 hv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = (_Float16)acc[i][j][r];
+            *reinterpret_cast<f16x4*>(so + rt * OS + (wn * C::TN + 16 * j + cq) * 2) = hv;
+          }
         }
       }
     }
@@ -502,7 +556,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
       if (rr < prow_end) {
         const uint4 v = *reinterpret_cast<const uint4*>(so + rr * OS + cb);
         const size_t row = (size_t)(ti.m0 + pass * PROWS + rr);
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Cout + row * ldc + col0) + cb) = v;
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Cout) + (row * ldc + col0) * OB + cb) = v;
       }
     }
   }
@@ -527,11 +581,11 @@ hipError_t launch(const void* a, const int32_t* perm, const int32_t* offsets, co
   const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
   if (ex.rows > 0)
     hipLaunchKernelGGL((grouped_gemm<C, PART, EQ, true>), dim3(grid), dim3(C::NTHR), 0, st,
-                       (const uint16_t*)a, perm, offsets, (const uint16_t*)b, (uint16_t*)c, H, E, k,
+                       (const uint16_t*)a, perm, offsets, (const uint16_t*)b, c, H, E, k,
                        Im, mu, n_tiles, T, ex);
   else
     hipLaunchKernelGGL((grouped_gemm<C, PART, EQ, false>), dim3(grid), dim3(C::NTHR), 0, st,
-                       (const uint16_t*)a, perm, offsets, (const uint16_t*)b, (uint16_t*)c, H, E, k,
+                       (const uint16_t*)a, perm, offsets, (const uint16_t*)b, c, H, E, k,
                        Im, mu, n_tiles, T, ex);
   return hipGetLastError();
 }

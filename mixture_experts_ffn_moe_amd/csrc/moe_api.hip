@@ -71,6 +71,14 @@ inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : M
 
 inline size_t elem_bytes(const Shape& s) { return s.bf16 ? 2 : 4; }
 
+static_assert(moe::kYBlock == MOE_Y_BLOCK, "y block of the header and the kernels");
+
+// A y buffer of `rows` rows: fp32 in the fp32 layer, block-scaled half in the
+// bf16 layers (moe_common.h).
+inline size_t y_bytes(const Shape& s, long long rows) {
+  return s.bf16 ? moe::y_half_bytes(rows, s.H) : (size_t)rows * s.H * 4;
+}
+
 void layout_of(const Shape& s, moe_workspace_layout* L) {
   const size_t R = (size_t)s.R();
   size_t o = 0;
@@ -82,7 +90,7 @@ void layout_of(const Shape& s, moe_workspace_layout* L) {
   L->perm = o;     o = align_up(o + R * 4);
   L->inv = o;      o = align_up(o + R * 4);
   L->h = o;        o = align_up(o + R * (size_t)s.mu * s.Im * elem_bytes(s));
-  L->y = o;        o = align_up(o + R * (size_t)s.H * elem_bytes(s));
+  L->y = o;        o = align_up(o + y_bytes(s, s.R()));
   L->scratch = o;
   o = align_up(o + std::max(moe::decode_scratch_bytes(), moe::route_hist_bytes(s)));
   L->total = o;
@@ -104,7 +112,7 @@ void shared_layout_of(const Shape& s, int Is, moe_shared_layout* L) {
   layout_of(s, &base);
   size_t o = base.total;
   L->hs = o; o = align_up(o + (size_t)s.T * Is * elem_bytes(s));
-  L->ys = o; o = align_up(o + (size_t)s.T * s.H * elem_bytes(s));
+  L->ys = o; o = align_up(o + y_bytes(s, s.T));
   L->total = o;
 }
 

@@ -74,6 +74,30 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// y, the down projection's output handed to the finalize, in the bf16 layers:
+// "block-scaled half".  Each row is cut into blocks of kYBlock columns; a
+// block stores its values as fp16 scaled by a power of two chosen from the
+// block's largest magnitude M (the values times 2^-e land in (-2^15, 2^15)
+// and round to at most 2^15, well within fp16's range), and e as one int8.  So y keeps 11 significant bits
+// (bf16 has 8) in the bytes of bf16 plus one per block: a bf16 y would be a
+// third rounding between the accumulator and the output, enough at outputs of
+// magnitude 4 and more to pass the bf16 bar of 2e-2.  Layout of a y buffer of
+// `rows` rows and H columns: values fp16 [rows, H], then exponents int8
+// [rows, H / kYBlock]; y[p][n] = values[p][n] * 2^exponents[p][n / kYBlock].
+constexpr int kYBlock = 256;
+inline size_t y_half_bytes(long long rows, int H) {
+  return (size_t)rows * H * 2 + (size_t)rows * (H / kYBlock);
+}
+// e for a block whose largest magnitude is M: floor(log2 M) - 14, clamped to
+// int8 (0 for M = 0; blocks below 2^-114 lose only digits far below any bar).
+__device__ __forceinline__ int yexp_of(float M) {
+  if (!(M > 0.0f)) return 0;
+  int e2;
+  (void)frexpf(M, &e2);  // M = f * 2^e2, f in [0.5, 1): floor(log2 M) = e2 - 1
+  const int e = e2 - 15;
+  return e < -128 ? -128 : (e > 127 ? 127 : e);
+}
+
 // Element loads/stores for the two supported element types.  bf16 tensors
 // are moved as raw 16-bit patterns.
 template <typename T> struct Elem;

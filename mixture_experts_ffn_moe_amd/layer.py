@@ -5,7 +5,7 @@ from __future__ import annotations
 import torch
 
 from ._lib import (MOE_BF16, moe_forward, moe_forward_shared, moe_get_shared_workspace_layout,
-                   moe_get_workspace_layout, moe_shared_workspace_size, moe_workspace_size)
+                   moe_get_workspace_layout, moe_shared_workspace_size, moe_workspace_size, y_nbytes)
 
 
 def _dtype(shape) -> torch.dtype:
@@ -34,7 +34,8 @@ def workspace_views(shape, ws: torch.Tensor) -> dict:
         "perm": view("perm", R, 4, torch.int32, (R,)),
         "inv": view("inv", R, 4, torch.int32, (R,)),
         "h": view("h", R * I, es, dt, (R, I)),
-        "y": view("y", R * H, es, dt, (R, H)),
+        # raw bytes: block-scaled half in the bf16 layers, fp32 in the fp32 layer
+        "y": ws[L["y"]:L["y"] + y_nbytes(shape, R)],
     }
 
 
@@ -71,5 +72,5 @@ class MoELayerBuffers:
             es = 2 if dt == torch.bfloat16 else 4
             T, H, Is = self.shape.T, self.shape.H, self.shared_Im
             v["hs"] = self.workspace[Ls["hs"]:Ls["hs"] + T * Is * es].view(dt).view(T, Is)
-            v["ys"] = self.workspace[Ls["ys"]:Ls["ys"] + T * H * es].view(dt).view(T, H)
+            v["ys"] = self.workspace[Ls["ys"]:Ls["ys"] + y_nbytes(self.shape, T)]
         return v

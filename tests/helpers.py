@@ -43,6 +43,41 @@ def shape_of(sp: mi.LayerSpec):
     return make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype, sp.renormalize)
 
 
+def y_buffer(sp, rows, device="cuda"):
+    """A y buffer (raw bytes) of `rows` rows for layer sp."""
+    import torch
+    from mixture_experts_ffn_moe_amd import y_nbytes
+    return torch.empty(y_nbytes(shape_of(sp), rows), dtype=torch.uint8, device=device)
+
+
+def decode_y(sp, buf, rows) -> np.ndarray:
+    """y values [rows, H] as float64 from a y buffer: fp32 for the fp32 layer;
+    for the bf16 layers block-scaled half, fp16 values [rows, H] then int8
+    exponents [rows, H / 256], y = value * 2^exponent (exact in float64)."""
+    raw = buf.cpu().numpy().view(np.uint8)
+    H = sp.H
+    if sp.dtype == mi.F32:
+        return raw.view(np.float32).reshape(rows, H).astype(np.float64)
+    vals = raw[:rows * H * 2].view(np.float16).reshape(rows, H).astype(np.float64)
+    exps = raw[rows * H * 2:rows * H * 2 + rows * (H // 256)].view(np.int8).reshape(rows, H // 256)
+    return vals * np.exp2(np.repeat(exps.astype(np.float64), 256, axis=1))
+
+
+def check_y_blocks(sp, buf, rows):
+    """Block-scaled half y: every block's largest |value| lies in [2^14, 2^15]
+    (scaled by the block's exponent into [2^14, 2^15), then rounded to fp16,
+    which can carry the largest up to 2^15), or the block is all zero with
+    exponent 0."""
+    raw = buf.cpu().numpy().view(np.uint8)
+    H = sp.H
+    vals = raw[:rows * H * 2].view(np.float16).reshape(rows, H // 256, 256).astype(np.float64)
+    exps = raw[rows * H * 2:rows * H * 2 + rows * (H // 256)].view(np.int8).reshape(rows, H // 256)
+    m = np.abs(vals).max(axis=2)
+    zero = m == 0
+    assert (exps[zero] == 0).all()
+    assert ((m[~zero] >= 2.0 ** 14) & (m[~zero] <= 2.0 ** 15)).all()
+
+
 def out_dtype(sp):
     import torch
     return torch.bfloat16 if sp.dtype == mi.BF16 else torch.float32

@@ -67,7 +67,7 @@ def test_workspace_size_and_layout(m):
     R = 4096 * 8
     assert L["total"] == m.moe_workspace_size(s)
     assert L["h"] - L["inv"] >= R * 4 and L["y"] - L["h"] >= R * 1536 * 2
-    assert L["total"] - L["y"] >= R * 4096 * 2
+    assert L["total"] - L["y"] >= R * 4096 * 2 + R * 16  # y: fp16 values + one exponent per 256 columns
     for v in L.values():
         assert v % 256 == 0
     # micro split does not change the size
@@ -210,7 +210,7 @@ def test_shared_workspace_layout(m):
     # the routed workspace comes first, unchanged; then hs [T, Is] and ys [T, H]
     assert Ls["hs"] == base
     assert Ls["ys"] - Ls["hs"] >= 4096 * 1536 * 2
-    assert Ls["total"] - Ls["ys"] >= 4096 * 4096 * 2
+    assert Ls["total"] - Ls["ys"] >= 4096 * 4096 * 2 + 4096 * 16  # ys: block-scaled half
     assert all(v % 256 == 0 for v in Ls.values())
 
 
