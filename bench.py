@@ -138,15 +138,36 @@ def relayout_two_micro(base, sp):
     return w1, w2
 
 
+SETTLE_S = 0.15  # the engine clock ramps for ~40 ms after the device has been idle
+
+
+def settle(fn, torch, seconds=SETTLE_S):
+    """Untimed calls of fn until the device has been busy with them for
+    `seconds` (in batches of 8, synchronised), so that the timed calls that
+    follow run at the clock the device holds under sustained load rather
+    than on its ramp from idle.  Returns the number of calls."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
 def time_forward(moe, torch, d, steps, warmup):
     """Median-free plain average over exactly `steps` timed calls of
-    moe_forward, bracketed by device synchronisation."""
+    moe_forward, bracketed by device synchronisation.  Before them: the
+    `warmup` untimed calls, then untimed calls until the clock has settled
+    (settle())."""
     sp = d["sp"]
     shape = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
     buf = moe.MoELayerBuffers(shape)
+    fwd = lambda: buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])  # noqa: E731
     for _ in range(warmup):
-        buf.forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"])
+        fwd()
     torch.cuda.synchronize()
+    settle(fwd, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
@@ -212,6 +233,7 @@ def time_two_dispatch(moe, torch, d, steps, warmup, ms_multi):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    settle(call, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -481,6 +503,7 @@ def time_shared(moe, torch, d, steps, warmup, cold=False):
         ts = timed_cold(torch, fwd, steps)
     else:
         torch.cuda.synchronize()
+        settle(fwd, torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
