@@ -548,6 +548,32 @@ def time_decode(moe, torch, steps, warmup):
                                    "added_ms": round(ms_sh - ms3, 5), "cache": "evicted before every call"}}
 
 
+def time_only_layer(moe, torch, name, steps, warmup):
+    """One of the 2-micro layers alone (the 1-micro layer's weights re-laid
+    micro-major; the skewed CFG batch with its own tokens and Zipf bias): the
+    one-call layer back to back and its five step-wise kernels."""
+    base = mi.make_layer(mi.spec("denoise_1micro"))
+    sp2 = mi.spec("denoise_2micro")
+    w1, w2 = relayout_two_micro(base, sp2)
+    if name == "denoise_2micro":
+        d = upload(mi.LayerInputs(sp2, base.x, base.wg, base.bias, w1, w2), torch)
+    else:
+        sp = mi.spec(name)
+        wg, bias = mi.make_router(sp)
+        d = upload(mi.LayerInputs(sp, mi.make_x(sp), wg, bias, w1, w2), torch)
+    del base, w1, w2
+    sp = d["sp"]
+    ms, _, buf = time_forward(moe, torch, d, steps, warmup)
+    counts = buf.views()["counts"].cpu().numpy()
+    del buf
+    kern, _ = time_kernels(moe, torch, d, steps, warmup)
+    tf = expert_flops(sp) / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 2), "tokens_per_s": round(sp.T / (ms * 1e-3), 1),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
+            "max_load": int(counts.max()), "empty_experts": int((counts == 0).sum())}
+
+
 def host_description() -> dict:
     """CPU model and the BLAS library numpy's float32 GEMMs run on."""
     model = None
@@ -611,6 +637,8 @@ def main(argv=None):
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--only-layer", choices=["denoise_2micro", "skewed_cfg"], default=None,
+                    help="time only this layer (its one-call layer and step-wise kernels), e.g. for a profile")
     ap.add_argument("--only-decode", action="store_true",
                     help="only time the AR-decode layer (for profiling) and print its numbers")
     args = ap.parse_args(argv)
@@ -632,6 +660,12 @@ def main(argv=None):
         dec = time_decode(moe, torch, max(args.steps, 50), args.warmup)
         log(f"decode {dec['ms'] * 1e3:.1f} us, {dec['GB_per_s']:.0f} GB/s")
         print(json.dumps({"decode": dec}), flush=True)
+        return 0
+
+    if args.only_layer:
+        res = time_only_layer(moe, torch, args.only_layer, args.steps, args.warmup)
+        log(f"{args.only_layer} {res['ms']:.4f} ms, {res['tflops']} TFLOP/s")
+        print(json.dumps({args.only_layer: res}), flush=True)
         return 0
 
     decode = None
