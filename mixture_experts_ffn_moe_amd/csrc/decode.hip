@@ -18,12 +18,11 @@
 //      fp32 rounding, top-k and weights (same rules as route.hip), expert
 //      counts and offsets, the stable permutation and its inverse, and the
 //      ascending list of active experts; workgroup 0 writes them out.
-//   3. decode_w13: one wave per (active expert, 16 columns of the
-//      micro-major intermediate), the waves' units dealt evenly over one
-//      workgroup per CU; each wave streams 16 gate and 16 up rows of w1 in
-//      whole 128-byte lines, re-lays them through LDS into MFMA B fragments
-//      (M = the expert's rows, padded to 16) and applies SwiGLU; h is rounded
-//      to bf16.
+//   3. decode_w13: one wave per (active expert, 8 columns of the micro-major
+//      intermediate), the waves' units dealt evenly over one workgroup per
+//      CU; each wave streams its 8 gate and 8 up rows of w1 straight to LDS in
+//      512-byte runs, reads them back as one MFMA B fragment (M = the
+//      expert's rows, padded to 16) and applies SwiGLU; h is rounded to bf16.
 //   4. decode_down_finalize: one workgroup per 16 output columns; its 16
 //      waves split the active experts (enough loads in flight per CU), stream
 //      the matching w2 rows the same way, and put
@@ -244,17 +243,16 @@ __device__ __forceinline__ void route_finish(
 }
 
 // ---------------------------------------------------------------------------
-// Weight streaming.  A wave reads 16 weight rows per 64-element k-step as two
-// loads of 8 rows x 128 bytes (eight lanes per row: every load covers whole
-// 128-byte lines, which HBM serves markedly faster than the 64-byte halves
-// the MFMA fragment layout would ask for), writes them to a per-wave LDS
-// buffer and reads them back in the 16x16x32 B-fragment layout (lane l: row
-// l % 16, 8 consecutive k of chunk l / 16).  Within a 128-byte row the 16-byte
-// chunks are XOR-swizzled by (row / 2) % 8, so the 16 lanes of one LDS phase
-// hit 16 bank groups on both sides.  The k order inside each MFMA is the one
-// the grouped GEMMs use, so h is the same bits on both paths.
+// Weight streaming of the down projection.  A wave reads 16 weight rows per
+// 64-element k-step as two loads of 8 rows x 128 bytes (eight lanes per row:
+// every load covers whole 128-byte lines, which HBM serves markedly faster
+// than the 64-byte halves the MFMA fragment layout would ask for), writes them
+// to a per-wave LDS buffer and reads them back in the 16x16x32 B-fragment
+// layout (lane l: row l % 16, 8 consecutive k of chunk l / 16).  Within a
+// 128-byte row the 16-byte chunks are XOR-swizzled by (row / 2) % 8, so the 16
+// lanes of one LDS phase hit 16 bank groups on both sides.  The k order inside
+// each MFMA is the one the grouped GEMMs use.
 constexpr int kStep = 64;        // k per LDS round trip
-constexpr int kStepsW13 = 4;     // k-steps of 64 whose loads are in flight together (w13)
 constexpr int kStepsDown = 4;    // the same for the down projection
 constexpr int kDownWaves = 16;   // waves of the down+finalize workgroup (they split the experts)
 
@@ -274,17 +272,26 @@ struct WaveRows {
 
 // ---------------------------------------------------------------------------
 // 3. gate|up + SwiGLU.  The work is a list of units, one per (active expert,
-// 16 intermediate columns) and then one per 16 columns of the shared expert;
-// a unit is one wave's stream of 16 gate and 16 up rows over all of H.  Each
-// of the kW13Blocks workgroups takes an equal contiguous share of the list
-// (the list length is known only on the device), its waves taking the share's
-// units in turn: every CU streams the same number of bytes (to one unit),
-// whatever the number of active experts.  (With one workgroup per 4 units, a
-// 43rd active expert or a shared expert put three workgroups on some CUs, and
-// those CUs, served the same share of HBM bandwidth as the rest, finished
-// ~25% later.)
+// 8 intermediate columns) and then one per 8 columns of the shared expert; a
+// unit is one wave's stream of its 8 gate and 8 up rows over all of H, the
+// 16 rows of one MFMA B fragment (output columns 0-7 gate, 8-15 up).  Each of
+// the kW13Blocks workgroups takes an equal contiguous share of the list (the
+// list length is known only on the device), its waves taking the share's
+// units in turn: every CU streams the same number of bytes to within one
+// 128 KB unit, whatever the number of active experts.  (A unit of 16 gate and
+// 16 up rows left half the waves idle at 42 active experts and, with the
+// shared expert's units added, put a ninth 256 KB unit on some CUs: +12 %.)
+//
+// The rows go straight to a per-wave LDS slot by direct-to-LDS copies, each
+// copy 2 rows x 512 contiguous bytes; a row's 16-byte chunk c sits at slot
+// position c ^ (row % 16), so the fragment reads (16 rows, one chunk column)
+// hit 16 bank groups.  Each MFMA takes the 32 k of one chunk column in the
+// same lane order as the grouped GEMMs, in ascending k: h is the same bits on
+// both paths.
 constexpr int kW13Waves = 16;    // waves per workgroup; a wave takes every 16th unit of its share
 constexpr int kW13Blocks = 256;  // one workgroup per CU
+constexpr int kSeg = 256;        // k per slot fill: 512 contiguous bytes of every row of the unit
+constexpr int kUnitCols = 8;     // gate (and up) rows per unit
 
 __global__ __launch_bounds__(kW13Waves * 64) void decode_w13(
     const uint16_t* __restrict__ x, const double* __restrict__ partial, const float* __restrict__ bias,
@@ -294,7 +301,8 @@ __global__ __launch_bounds__(kW13Waves * 64) void decode_w13(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets_out, int32_t* __restrict__ perm_out,
     int32_t* __restrict__ inv, int32_t* __restrict__ active_out, int renorm) {
   static_assert(kW13Waves * 64 == kDecT * kMaxExperts, "routing: one thread per (token, expert)");
-  __shared__ __attribute__((aligned(16))) char buf[kW13Waves][2][2048];  // per wave: gate, up
+  constexpr int kSlot = 2 * kUnitCols * kSeg * 2;  // bytes: 16 rows x 512
+  __shared__ __attribute__((aligned(1024))) char buf[kW13Waves][kSlot];
   __shared__ RouteLds rs;
   route_finish(partial, bias, T, E, k, renorm != 0, blockIdx.x == 0, logits, ids, topw, counts, offsets_out, perm_out,
                inv, active_out, rs);
@@ -303,11 +311,15 @@ __global__ __launch_bounds__(kW13Waves * 64) void decode_w13(
   const int* perm = rs.perm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  const int ue = mu * Im / 16;                      // units per routed expert
+  const int fr = lane & 15, g4 = lane >> 4;
+  const int ue = mu * Im / kUnitCols;  // units per routed expert
   const int routed_units = active[kMaxExperts] * ue;
-  const int units = routed_units + (w1s != nullptr ? Is / 16 : 0);
+  const int units = routed_units + (w1s != nullptr ? Is / kUnitCols : 0);
   const int u_end = (int)((long long)(blockIdx.x + 1) * units / gridDim.x);
+  const uint32_t slot = (uint32_t)(uintptr_t)buf[wave];
+  // copy q of a fill: unit row 2q + lane/32, slot position lane % 32 holding
+  // the row's chunk (lane % 32) ^ (row % 16)
+  const int crow = lane >> 5, cpos = lane & 31;
   for (int u = (int)((long long)blockIdx.x * units / gridDim.x) + wave; u < u_end; u += kW13Waves) {
     int n, c0, i0, Imx, ldh;
     const uint16_t* arow;
@@ -316,74 +328,64 @@ __global__ __launch_bounds__(kW13Waves * 64) void decode_w13(
     if (u >= routed_units) {
       // shared expert: every token, in order
       n = T;
-      c0 = (u - routed_units) * 16;
+      c0 = (u - routed_units) * kUnitCols;
       i0 = c0;
       Imx = Is;
       ldh = Is;
-      arow = x + (size_t)min(fr, n - 1) * H + fk;
+      arow = x + (size_t)min(fr, n - 1) * H + g4 * 8;
       wbase = w1s;
       hout = hs;
     } else {
       const int e = active[u / ue];
       const int seg = offsets[e];
       n = offsets[e + 1] - seg;
-      c0 = (u % ue) * 16;  // column in [0, mu*Im)
+      c0 = (u % ue) * kUnitCols;  // column in [0, mu*Im)
       const int micro = c0 / Im;
       i0 = c0 - micro * Im;
       Imx = Im;
       ldh = mu * Im;
-      arow = x + (size_t)(perm[seg + min(fr, n - 1)] / k) * H + fk;
+      // rows past the expert's repeat its last token (finite values in MFMA
+      // rows that are never stored)
+      arow = x + (size_t)(perm[seg + min(fr, n - 1)] / k) * H + g4 * 8;
       wbase = w1 + (size_t)(micro * E + e) * 2 * Im * H;
       hout = h + (size_t)seg * ldh;
     }
-    const WaveRows wr(lane);
-    char* gb = buf[wave][0];
-    char* ub = buf[wave][1];
-
-    const bool row_ok = fr < n;
-    // rows lane/8 and 8 + lane/8 of the gate and up blocks, chunk lane % 8
-    const uint16_t* g0 = wbase + (size_t)(i0 + (lane >> 3)) * H + (lane & 7) * 8;
-    const uint16_t* u0 = wbase + (size_t)(Imx + i0 + (lane >> 3)) * H + (lane & 7) * 8;
-    const size_t r8 = (size_t)8 * H;
-
-    f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < H; k0 += kStep * kStepsW13) {
-      uint4 gv[kStepsW13][2], uv[kStepsW13][2], av[kStepsW13][2];
+    // unit row r < 8: gate row i0 + r; r >= 8: up row Imx + i0 + r - 8
+    const uint16_t* sb = uniform_ptr(wbase + (size_t)i0 * H);
+    uint32_t voff[kUnitCols];
 #pragma unroll
-      for (int q = 0; q < kStepsW13; ++q) {
-        const int kk = k0 + kStep * q;
-        gv[q][0] = *reinterpret_cast<const uint4*>(g0 + kk);
-        gv[q][1] = *reinterpret_cast<const uint4*>(g0 + r8 + kk);
-        uv[q][0] = *reinterpret_cast<const uint4*>(u0 + kk);
-        uv[q][1] = *reinterpret_cast<const uint4*>(u0 + r8 + kk);
-        // rows past the expert's are zero: only real rows are loaded
-        av[q][0] = row_ok ? *reinterpret_cast<const uint4*>(arow + kk) : make_uint4(0, 0, 0, 0);
-        av[q][1] = row_ok ? *reinterpret_cast<const uint4*>(arow + kk + 32) : make_uint4(0, 0, 0, 0);
-      }
+    for (int q = 0; q < kUnitCols; ++q) {
+      const int r = 2 * q + crow;
+      const int wr = r < kUnitCols ? r : Imx + r - kUnitCols;
+      voff[q] = ((uint32_t)wr * (uint32_t)H + (uint32_t)((cpos ^ (r & 15)) * 8)) * 2u;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < H; k0 += kSeg) {
+      // the fragment reads of the previous fill are done before the slot is refilled
+      __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < kStepsW13; ++q) {
-        *reinterpret_cast<uint4*>(gb + wr.wr0) = gv[q][0];
-        *reinterpret_cast<uint4*>(gb + wr.wr1) = gv[q][1];
-        *reinterpret_cast<uint4*>(ub + wr.wr0) = uv[q][0];
-        *reinterpret_cast<uint4*>(ub + wr.wr1) = uv[q][1];
-        const uint4 gf0 = *reinterpret_cast<const uint4*>(gb + wr.rd0);
-        const uint4 gf1 = *reinterpret_cast<const uint4*>(gb + wr.rd1);
-        const uint4 uf0 = *reinterpret_cast<const uint4*>(ub + wr.rd0);
-        const uint4 uf1 = *reinterpret_cast<const uint4*>(ub + wr.rd1);
-        uint4 a0 = av[q][0], a1 = av[q][1];
-        const bf16x8 A0 = __builtin_bit_cast(bf16x8, a0), A1 = __builtin_bit_cast(bf16x8, a1);
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, gf0), accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8, uf0), accu, 0, 0, 0);
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, gf1), accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8, uf1), accu, 0, 0, 0);
+      for (int q = 0; q < kUnitCols; ++q) dma16(slot + q * 1024u, sb + k0, voff[q]);
+      uint4 av[kSeg / 32];
+#pragma unroll
+      for (int j = 0; j < kSeg / 32; ++j) av[j] = *reinterpret_cast<const uint4*>(arow + k0 + 32 * j);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kSeg / 32; ++j) {
+        const uint4 b = *reinterpret_cast<const uint4*>(buf[wave] + fr * (kSeg * 2) + (((4 * j + g4) ^ fr) * 16));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[j]), __builtin_bit_cast(bf16x8, b),
+                                                      acc, 0, 0, 0);
       }
     }
-    // D layout: register r holds row 4*(lane/16) + r, column lane%16
+    // D layout: register r holds row 4*(lane/16) + r, column lane%16 (gate
+    // columns 0-7, their up columns 8-15)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 4 * (lane >> 4) + r;
-      if (row < n)
-        hout[(size_t)row * ldh + c0 + fr] = float_to_bf16_bits(silu_f32(accg[r]) * accu[r]);
+      const float up = __shfl_xor(acc[r], 8);
+      const int row = 4 * g4 + r;
+      if (fr < kUnitCols && row < n)
+        hout[(size_t)row * ldh + c0 + fr] = float_to_bf16_bits(silu_f32(acc[r]) * up);
     }
   }  // units of this wave
 }
@@ -497,7 +499,7 @@ bool decode_shared_supported(int Is) {
 
 bool decode_supported(const Shape& s) {
   return s.bf16 && s.T >= 1 && s.T <= kDecT && s.k <= kMaxK && (s.H % (kSplit * 128)) == 0 &&
-         (s.Im % 64) == 0 && (s.mu * s.Im) % 64 == 0 && (s.H % (kStep * kStepsW13)) == 0 &&
+         (s.Im % 64) == 0 && (s.mu * s.Im) % 64 == 0 && (s.H % kSeg) == 0 &&
          (s.Im % (kStep * kStepsDown)) == 0 && (s.H % 16) == 0;
 }
 

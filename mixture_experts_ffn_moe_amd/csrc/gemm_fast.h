@@ -63,22 +63,6 @@ __device__ __forceinline__ int swz(int row) {
   return (row / (16 / CPR)) % CPR;
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  // s_waitcnt with only vmcnt restricted (expcnt = 7, lgkmcnt = 15: no wait)
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One direct-to-LDS load: every lane copies 16 bytes from sbase + voff (bytes)
-// to LDS address lds + 16 * lane.  Issued as inline asm so the compiler's
-// wait-count tracking does not serialise the pipeline: callers wait on vmcnt
-// and barrier themselves before reading the destination.
-__device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-
 // Workgroup barrier for the k loop.  __syncthreads() carries a memory fence
 // that waits for every outstanding global load, including the direct-to-LDS
 // copies still in flight for later k-tiles; this one waits only for the

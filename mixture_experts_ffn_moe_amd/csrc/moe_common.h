@@ -43,6 +43,36 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // s_waitcnt with only vmcnt restricted (expcnt = 7, lgkmcnt = 15: no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One direct-to-LDS load: every lane copies 16 bytes from sbase + voff (bytes)
+// to LDS address lds + 16 * lane.  Issued as inline asm so the compiler's
+// wait-count tracking does not serialise the pipeline: callers wait on vmcnt
+// and barrier themselves before reading the destination.  lds and sbase must
+// be wave-uniform (scalar registers).
+__device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// A pointer the caller knows to be wave-uniform, moved to scalar registers
+// (lane 0's value).  readfirstlane takes and returns int: each 32-bit half is
+// taken back to uint32_t before it is widened, so the low half is
+// zero-extended (a sign-extended low half with bit 31 set would turn the
+// address into 0xffffffff........).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 // Orderable 32-bit key of a float: unsigned order equals numeric order and
 // -0.0 maps to the key of +0.0; every finite float's key is nonzero.
 __device__ __forceinline__ uint32_t orderable(float f) {

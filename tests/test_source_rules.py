@@ -10,6 +10,13 @@ register outputs; loads into registers are written as ordinary C++ loads,
 which the compiler tracks.  This test keeps it that way, and checks that
 an asm statement that sets m0 (the LDS address of a direct-to-LDS copy)
 names m0 as clobbered.
+
+The readfirstlane builtin takes and returns int.  Widened straight to a
+64-bit type, its result is sign-extended: the low half of an address with
+bit 31 set becomes 0xffffffff........, and a copy from that address faults
+the GPU.  Uniform pointers go through uniform_ptr (moe_common.h), which
+takes each half back to uint32_t first; no other source widens the
+builtin's result directly.
 """
 import glob
 import os
@@ -66,6 +73,32 @@ def m0_unclobbered(src):
     compiler could otherwise keep a live value of its own in m0)."""
     return [t for t, _, clob in asm_blocks(src)
             if re.search(r"\bs_mov_b32\s+m0\b", t) and '"m0"' not in clob]
+
+
+_WIDE = r"(?:u?int64_t|size_t|uintptr_t|intptr_t|(?:unsigned\s+)?long(?:\s+long)?)"
+_RFL_WIDENED = re.compile(r"\(\s*" + _WIDE + r"\s*\)\s*__builtin_amdgcn_readfirstlane\s*\(")
+
+
+def readfirstlane_widened(src):
+    """Casts of readfirstlane's int result straight to a 64-bit type."""
+    src = re.sub(r"//[^\n]*", "", src)
+    return _RFL_WIDENED.findall(src)
+
+
+def test_rule_detects_a_sign_extended_readfirstlane():
+    bad = "const uint64_t lo = (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)v);"
+    assert readfirstlane_widened(bad)
+    assert readfirstlane_widened(bad.replace("(uint64_t)", "(size_t) "))
+    good = "const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);"
+    assert not readfirstlane_widened(good)
+
+
+def test_no_sign_extended_readfirstlane():
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+    for f in files:
+        assert not readfirstlane_widened(open(f).read()), f"{os.path.basename(f)}: readfirstlane widened to 64 bits"
+    common = open(os.path.join(CSRC, "moe_common.h")).read()
+    assert "uniform_ptr" in common
 
 
 def test_rule_detects_a_register_output_load():
