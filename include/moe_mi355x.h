@@ -36,15 +36,16 @@
  * fp32 in an MOE_F32 layer.  In an MOE_BF16 layer it is "block-scaled half":
  * each row is cut into blocks of MOE_Y_BLOCK columns; the buffer holds the
  * values as fp16 [rows, H] followed by one int8 exponent per block
- * [rows, H / MOE_Y_BLOCK], and y[p, n] = value[p, n] * 2^exponent[p, n / MOE_Y_BLOCK].
+ * [rows, ceil(H / MOE_Y_BLOCK)] (the last block of a row is partial when
+ * H % MOE_Y_BLOCK != 0), and y[p, n] = value[p, n] * 2^exponent[p, n / MOE_Y_BLOCK].
  * A block's exponent is floor(log2 M) - 14 for its largest magnitude M (0 for
  * an all-zero block), so every value keeps 11 significant bits in the bytes of
  * bf16 plus one per block.  (A bf16 y would be a third rounding between the
  * fp32 accumulator and the output; at outputs of magnitude 4 and more that
  * takes the error past the bf16 bar of 2e-2.)  Size: MOE_Y_BYTES(dtype, rows, H).
  *
- * Envelope (MOE_ERR_UNSUPPORTED outside it): 1 <= E <= 64, H % 256 == 0,
- * Im % 128 == 0, R < 2^31, every size in elements < 2^31, one expert's w1
+ * Envelope (MOE_ERR_UNSUPPORTED outside it): 1 <= E <= 64, H % 64 == 0,
+ * Im % 32 == 0, R < 2^31, every size in elements < 2^31, one expert's w1
  * block (2*Im*H elements of 2 bytes) < 4 GiB.
  */
 #ifndef MOE_MI355X_H
@@ -70,7 +71,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Columns per exponent of a block-scaled half y, and the bytes of a y buffer. */
 #define MOE_Y_BLOCK 256
 #define MOE_Y_BYTES(dtype, rows, H)                                                        \
-  ((dtype) == MOE_BF16 ? (size_t)(rows) * (size_t)(H) * 2 + (size_t)(rows) * ((H) / MOE_Y_BLOCK) \
+  ((dtype) == MOE_BF16 ? (size_t)(rows) * (size_t)(H) * 2 + (size_t)(rows) * (((H) + MOE_Y_BLOCK - 1) / MOE_Y_BLOCK) \
                        : (size_t)(rows) * (size_t)(H) * 4)
 
 typedef struct {

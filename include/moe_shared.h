@@ -29,7 +29,7 @@
  * layer; MOE_Y_BYTES(dtype, T, H) bytes).  Sums are in fp32 and every dtype
  * result is rounded once.
  *
- * Envelope, beside moe_mi355x.h's: Is % 128 == 0, T*Is < 2^31, the w1s block
+ * Envelope, beside moe_mi355x.h's: Is % 32 == 0, T*Is < 2^31, the w1s block
  * (2*Is*H elements of 2 bytes) < 4 GiB; otherwise MOE_ERR_UNSUPPORTED.
  * Is <= 0 is MOE_ERR_INVALID_ARG.
  */

@@ -152,7 +152,7 @@ def y_nbytes(shape, rows: int) -> int:
     the fp32 layer."""
     H = shape.H
     if shape.dtype == MOE_BF16:
-        return rows * H * 2 + rows * (H // Y_BLOCK)
+        return rows * H * 2 + rows * (-(-H // Y_BLOCK))
     return rows * H * 4
 
 

@@ -32,7 +32,7 @@ struct YRow {
                                               float (&v)[8]) {
     typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
     const f16x8 h = *reinterpret_cast<const f16x8*>(y + row * H + c);
-    const int e = ye[row * (H / kYBlock) + c / kYBlock];
+    const int e = ye[row * ((H + kYBlock - 1) / kYBlock) + c / kYBlock];  // a partial last block when H % kYBlock != 0
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = ldexpf((float)h[q], e);
   }

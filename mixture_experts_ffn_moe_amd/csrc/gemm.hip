@@ -154,6 +154,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(
 //    output tile leaves in one pass per 80-row block of waves).
 using W13Cfg = fast::Cfg<fast::kW13, 320, 256, 64, 2, 4, 2, 2>;
 using DownCfg = fast::Cfg<fast::kDown, 320, 256, 64, 2, 4, 2, 2>;
+// Narrower shapes of the envelope (none of the benchmark's layers): w13 tiles
+// of 32 gate + 32 up columns when Im (or the shared width) is not a multiple
+// of 128, and down k-steps of 32 when it is not a multiple of 64, so that no
+// k-step crosses a micro-shard boundary (256-row tiles: a 1 KB copy covers 16
+// rows of 64 bytes, and 320 rows do not split evenly over the 8 waves).
+using W13NarrowCfg = fast::Cfg<fast::kW13, 320, 64, 64, 2, 4, 2, 2>;
+using DownK32Cfg = fast::Cfg<fast::kDown, 256, 256, 32, 2, 4, 2, 2>;
+
+inline bool wide_w13(int w) { return w % W13Cfg::HCOLS == 0; }
+inline bool deep_down(int w) { return w % DownCfg::BK == 0; }
 
 
 inline unsigned grid_size(long long tiles) {
@@ -166,7 +176,8 @@ inline unsigned grid_size(long long tiles) {
 hipError_t launch_w13_swiglu(const Shape& s, const void* x, const int32_t* perm,
                              const int32_t* offsets, const void* w1, void* h, hipStream_t st) {
   if (s.bf16) {
-    return fast::launch<W13Cfg>(x, perm, offsets, w1, h, s.T, s.H, s.E, s.k, s.Im, s.mu, st);
+    if (wide_w13(s.Im)) return fast::launch<W13Cfg>(x, perm, offsets, w1, h, s.T, s.H, s.E, s.k, s.Im, s.mu, st);
+    return fast::launch<W13NarrowCfg>(x, perm, offsets, w1, h, s.T, s.H, s.E, s.k, s.Im, s.mu, st);
   } else {
     const int n_tiles = s.mu * (s.Im / 32);
     const unsigned g = grid_size(fast::max_m_tiles(s.R(), s.E, FBM) * n_tiles);
@@ -180,20 +191,25 @@ hipError_t launch_w13_swiglu_with_dense(const Shape& s, const void* x, const int
                                         const int32_t* offsets, const void* w1, void* h,
                                         const void* w1d, void* hd, int wd, hipStream_t st) {
   const fast::Extra ex{(const uint16_t*)x, (const uint16_t*)w1d, hd, s.T, wd};
-  return fast::launch<W13Cfg>(x, perm, offsets, w1, h, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
+  if (wide_w13(s.Im) && wide_w13(wd))
+    return fast::launch<W13Cfg>(x, perm, offsets, w1, h, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
+  return fast::launch<W13NarrowCfg>(x, perm, offsets, w1, h, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
 }
 
 hipError_t launch_down_with_dense(const Shape& s, const void* h, const int32_t* offsets,
                                   const void* w2, void* y, const void* hd, const void* w2d,
                                   void* yd, int wd, hipStream_t st) {
   const fast::Extra ex{(const uint16_t*)hd, (const uint16_t*)w2d, yd, s.T, wd};
-  return fast::launch<DownCfg>(h, nullptr, offsets, w2, y, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
+  if (deep_down(s.Im) && deep_down(wd))
+    return fast::launch<DownCfg>(h, nullptr, offsets, w2, y, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
+  return fast::launch<DownK32Cfg>(h, nullptr, offsets, w2, y, s.T, s.H, s.E, s.k, s.Im, s.mu, st, ex);
 }
 
 hipError_t launch_down(const Shape& s, const void* h, const int32_t* offsets, const void* w2,
                        void* y, hipStream_t st) {
   if (s.bf16) {
-    return fast::launch<DownCfg>(h, nullptr, offsets, w2, y, s.T, s.H, s.E, s.k, s.Im, s.mu, st);
+    if (deep_down(s.Im)) return fast::launch<DownCfg>(h, nullptr, offsets, w2, y, s.T, s.H, s.E, s.k, s.Im, s.mu, st);
+    return fast::launch<DownK32Cfg>(h, nullptr, offsets, w2, y, s.T, s.H, s.E, s.k, s.Im, s.mu, st);
   } else {
     const int n_tiles = s.H / FBN;
     const unsigned g = grid_size(fast::max_m_tiles(s.R(), s.E, FBM) * n_tiles);

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
 
   // XS: the launch has an extra dense segment (a separate instantiation, so
   // the routed-only kernel carries none of its tile logic)
-  const int x_ntiles = XS ? ((C::MODE == kW13) ? ex.w / C::HCOLS : H / C::BN) : 0;
+  const int x_ntiles = XS ? ((C::MODE == kW13) ? ex.w / C::HCOLS : (H + C::BN - 1) / C::BN) : 0;
   const Tile ti = decode_wave<C::BM, EQ, XS>(offsets, E, n_tiles, dense_rows, ex.rows, x_ntiles);
   if (!ti.valid) return;
   // a tile of the extra dense segment: its own A, B, C and width, one micro
@@ -288,6 +288,10 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const int c = lpos ^ swz<C::CPR>(row);
     int wrow = row;
     if (C::MODE == kW13) wrow = row < C::BN / 2 ? n0 + row : Im + n0 + (row - C::BN / 2);
+    // down: the last n-tile may reach past H (H % BN != 0); its rows past H
+    // copy row H - 1 again, whose output columns are never stored (and, being
+    // a copy of a stored column, leave the row's block maximum unchanged)
+    else wrow = min(row, H - 1 - n0);
     b_off[i] = ((uint32_t)wrow * b_ld + c * 8) * 2u;
   }
   constexpr int A_SLOT = C::BM * C::BK, B_SLOT = C::BN * C::BK;  // elements
@@ -502,7 +506,7 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = ldexpf(acc[i][j][r], -e);
       if (wn == 0 && lane < 16 && tr < rows)
-        ye[(size_t)(ti.m0 + tr) * (size_t)(ldc / kYBlock) + col0 / kYBlock] = (int8_t)e;
+        ye[(size_t)(ti.m0 + tr) * (size_t)((ldc + kYBlock - 1) / kYBlock) + col0 / kYBlock] = (int8_t)e;
     }
   }
 
@@ -537,7 +541,8 @@ __global__ __launch_bounds__(C::NTHR, 1) void grouped_gemm(
     const int prow_end = min(rows - pass * PROWS, PROWS);
     for (int r0 = wave * RPW; r0 < prow_end; r0 += C::NW * RPW) {
       const int rr = r0 + lane / LPR;
-      if (rr < prow_end) {
+      // down: columns past H (a partial last n-tile) are not stored
+      if (rr < prow_end && (C::MODE == kW13 || col0 + cb / OB < ldc)) {
         const uint4 v = *reinterpret_cast<const uint4*>(so + rr * OS + cb);
         const size_t row = (size_t)(ti.m0 + pass * PROWS + rr);
         *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Cout) + (row * ldc + col0) * OB + cb) = v;
@@ -558,8 +563,8 @@ template <class C, bool PART = true, bool EQ = true>
 hipError_t launch(const void* a, const int32_t* perm, const int32_t* offsets, const void* b,
                   void* c, int T, int H, int E, int k, int Im, int mu, hipStream_t st,
                   Extra ex = Extra{nullptr, nullptr, nullptr, 0, 0}) {
-  const int n_tiles = (C::MODE == kW13) ? mu * (Im / C::HCOLS) : H / C::BN;
-  const int x_ntiles = (C::MODE == kW13) ? ex.w / C::HCOLS : H / C::BN;
+  const int n_tiles = (C::MODE == kW13) ? mu * (Im / C::HCOLS) : (H + C::BN - 1) / C::BN;
+  const int x_ntiles = (C::MODE == kW13) ? ex.w / C::HCOLS : (H + C::BN - 1) / C::BN;
   const long long tiles = max_m_tiles((long long)T * k, E, C::BM) * n_tiles +
                           (long long)((ex.rows + C::BM - 1) / C::BM) * x_ntiles;
   const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);

@@ -36,7 +36,9 @@ moe_status check_shape(const moe_shape* sh, Shape* out) {
   if (s.dtype != MOE_F32 && s.dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (s.renormalize != 0 && s.renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (s.E > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
-  if (s.H % 256 != 0 || s.Im % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  // k-steps of 64 over H (w13) and of 32 over Im (down); w13 output tiles of
+  // 32 columns; down output tiles of 64 columns (the fp32 path)
+  if (s.H % 64 != 0 || s.Im % 32 != 0) return MOE_ERR_UNSUPPORTED;
   const long long R = (long long)s.T * s.k;
   const long long I = (long long)s.micro_count * s.Im;
   const long long lim = (1ll << 31) - 1;
@@ -99,7 +101,7 @@ void layout_of(const Shape& s, moe_workspace_layout* L) {
 // The shared expert's width against the envelope (moe_shared.h).
 moe_status check_shared(const Shape& s, int32_t Is) {
   if (Is <= 0) return MOE_ERR_INVALID_ARG;
-  if (Is % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (Is % 32 != 0) return MOE_ERR_UNSUPPORTED;
   const long long lim = (1ll << 31) - 1;
   if ((long long)s.T * Is > lim || 2ll * Is * s.H > lim || 4ll * Is * s.H > 0xffffffffll)
     return MOE_ERR_UNSUPPORTED;

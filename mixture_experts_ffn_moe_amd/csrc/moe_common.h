@@ -113,10 +113,11 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // third rounding between the accumulator and the output, enough at outputs of
 // magnitude 4 and more to pass the bf16 bar of 2e-2.  Layout of a y buffer of
 // `rows` rows and H columns: values fp16 [rows, H], then exponents int8
-// [rows, H / kYBlock]; y[p][n] = values[p][n] * 2^exponents[p][n / kYBlock].
+// [rows, ceil(H / kYBlock)] (a partial last block when H % kYBlock != 0);
+// y[p][n] = values[p][n] * 2^exponents[p][n / kYBlock].
 constexpr int kYBlock = 256;
 inline size_t y_half_bytes(long long rows, int H) {
-  return (size_t)rows * H * 2 + (size_t)rows * (H / kYBlock);
+  return (size_t)rows * H * 2 + (size_t)rows * ((H + kYBlock - 1) / kYBlock);
 }
 // e for a block whose largest magnitude is M: floor(log2 M) - 14, clamped to
 // int8 (0 for M = 0; blocks below 2^-114 lose only digits far below any bar).

@@ -52,9 +52,10 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 // Logit tile of kTokTile tokens x 64 experts on the fp64 matrix pipe
 // (v_mfma_f64_16x16x4_f64, exact products, fp64 sums).  Sixteen waves, four
 // per SIMD (one wave alone cannot keep the matrix pipe busy, and four hide the
-// activation loads from HBM better than two): wave w covers the hidden eighth
-// hw = w % 8, [hw*H/8, (hw+1)*H/8), for the 16-expert tiles q = 2*(w/8) and
-// 2*(w/8)+1; lane (t = lane%16, g = lane/16) holds x[t][h0 + 8g + m] and
+// activation loads from HBM better than two): wave w covers the hidden part
+// hw = w % 8 -- the 32-wide chunks [hw*nc/8, (hw+1)*nc/8) of the nc = H/32
+// chunks, an eighth of H when H % 256 == 0 -- for the 16-expert tiles
+// q = 2*(w/8) and 2*(w/8)+1; lane (t = lane%16, g = lane/16) holds x[t][h0 + 8g + m] and
 // wg[16q + t][h0 + 8g + m] as the m-th MFMA's A and B elements, so the 8
 // MFMAs of a 32-wide chunk sum every h of the chunk exactly once.  The eight
 // partials are added in a fixed order, so the logits are reproducible run to
@@ -79,8 +80,9 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
   const int hw = wave % kHParts, eh = wave / kHParts;  // hidden part, expert half
   const int t0 = blockIdx.x * kTokTile;
   const int tl = lane & 15, g = lane >> 4;
-  const int hq = H / kHParts;
-  const int hb = hw * hq;
+  const int nc = H / 32;  // 32-wide chunks of the hidden dimension
+  const int cb = hw * nc / kHParts, ce = (hw + 1) * nc / kHParts;
+  const int hb = cb * 32, hq = (ce - cb) * 32;  // this part's first column and width (hq may be 0)
 
   if (tid < kMaxExperts) hcnt[tid] = 0;  // ordered before its use by the barriers below
 
@@ -99,7 +101,9 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
   for (int q = 0; q < 2; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // chunk loads are double-buffered: chunk c+32 is in flight while the
-  // 16 MFMAs of chunk c run (hq = H / kHParts is a multiple of 32)
+  // 16 MFMAs of chunk c run (hq is a multiple of 32; the first chunk's load,
+  // issued before the loop, stays inside the row even when hq == 0, since
+  // cb < nc)
   float xv[2][8], wv[2][2][8];
   auto load_chunk = [&](int c, int b) {
     load8(xrow + c, xv[b]);

@@ -53,14 +53,15 @@ def y_buffer(sp, rows, device="cuda"):
 def decode_y(sp, buf, rows) -> np.ndarray:
     """y values [rows, H] as float64 from a y buffer: fp32 for the fp32 layer;
     for the bf16 layers block-scaled half, fp16 values [rows, H] then int8
-    exponents [rows, H / 256], y = value * 2^exponent (exact in float64)."""
+    exponents [rows, ceil(H / 256)], y = value * 2^exponent (exact in float64)."""
     raw = buf.cpu().numpy().view(np.uint8)
     H = sp.H
     if sp.dtype == mi.F32:
         return raw.view(np.float32).reshape(rows, H).astype(np.float64)
+    nb = -(-H // 256)
     vals = raw[:rows * H * 2].view(np.float16).reshape(rows, H).astype(np.float64)
-    exps = raw[rows * H * 2:rows * H * 2 + rows * (H // 256)].view(np.int8).reshape(rows, H // 256)
-    return vals * np.exp2(np.repeat(exps.astype(np.float64), 256, axis=1))
+    exps = raw[rows * H * 2:rows * H * 2 + rows * nb].view(np.int8).reshape(rows, nb)
+    return vals * np.exp2(np.repeat(exps.astype(np.float64), 256, axis=1)[:, :H])
 
 
 def check_y_blocks(sp, buf, rows):
@@ -70,9 +71,10 @@ def check_y_blocks(sp, buf, rows):
     exponent 0."""
     raw = buf.cpu().numpy().view(np.uint8)
     H = sp.H
-    vals = raw[:rows * H * 2].view(np.float16).reshape(rows, H // 256, 256).astype(np.float64)
-    exps = raw[rows * H * 2:rows * H * 2 + rows * (H // 256)].view(np.int8).reshape(rows, H // 256)
-    m = np.abs(vals).max(axis=2)
+    nb = -(-H // 256)
+    vals = raw[:rows * H * 2].view(np.float16).reshape(rows, H).astype(np.float64)
+    exps = raw[rows * H * 2:rows * H * 2 + rows * nb].view(np.int8).reshape(rows, nb)
+    m = np.stack([np.abs(vals[:, 256 * b:256 * (b + 1)]).max(axis=1) for b in range(nb)], axis=1)
     zero = m == 0
     assert (exps[zero] == 0).all()
     assert ((m[~zero] >= 2.0 ** 14) & (m[~zero] <= 2.0 ** 15)).all()

@@ -83,8 +83,10 @@ def test_workspace_size_and_layout(m):
     ((64, 256, 8, 0, 128, 1), "MOE_ERR_INVALID_ARG"),     # k < 1
     ((-1, 256, 8, 2, 128, 1), "MOE_ERR_INVALID_ARG"),     # T < 0
     ((64, 256, 8, 2, 128, 0), "MOE_ERR_INVALID_ARG"),     # no micro-shard
-    ((64, 200, 8, 2, 128, 1), "MOE_ERR_UNSUPPORTED"),     # H not a multiple of 256
-    ((64, 256, 8, 2, 96, 1), "MOE_ERR_UNSUPPORTED"),      # Im not a multiple of 128
+    ((64, 200, 8, 2, 128, 1), "MOE_ERR_UNSUPPORTED"),     # H not a multiple of 64
+    ((64, 288, 8, 2, 128, 1), "MOE_ERR_UNSUPPORTED"),     # H a multiple of 32, not of 64
+    ((64, 256, 8, 2, 48, 1), "MOE_ERR_UNSUPPORTED"),      # Im not a multiple of 32
+    ((64, 256, 8, 2, 80, 2), "MOE_ERR_UNSUPPORTED"),      # Im a multiple of 16, not of 32
     ((1 << 28, 4096, 64, 8, 128, 1), "MOE_ERR_UNSUPPORTED"),  # T*k*H beyond 2^31
 ])
 def test_shape_validation(m, args, code):
@@ -202,6 +204,27 @@ def test_binding_checks_tensors_before_the_call(m):
 # ---------------------------------------------------------------- shared expert (moe_shared.h)
 
 
+@pytest.mark.parametrize("H,Im,mu", [(320, 96, 1), (64, 32, 3), (448, 160, 2), (4096, 1536, 1)])
+def test_envelope_accepts_multiples_of_64_and_32(m, H, Im, mu):
+    """H % 64 == 0 and Im % 32 == 0 are inside the envelope (the bf16 kernels
+    then take the narrow tile shapes or a partial last output tile)."""
+    for dt in ("bf16", "f32"):
+        s = m.make_shape(16, H, 8, 2, Im, mu, dt)
+        assert m.moe_workspace_size(s) > 0
+
+
+@pytest.mark.parametrize("H", [64, 192, 256, 320, 4096])
+def test_y_layout_size(m, H):
+    """Block-scaled half y: fp16 values then one int8 exponent per started
+    block of 256 columns (MOE_Y_BYTES); fp32 y in the fp32 layer."""
+    rows = 7
+    nb = (H + 255) // 256
+    assert m.y_nbytes(m.make_shape(4, H, 8, 2, 64, 1, "bf16"), rows) == rows * H * 2 + rows * nb
+    assert m.y_nbytes(m.make_shape(4, H, 8, 2, 64, 1, "f32"), rows) == rows * H * 4
+    L = m.moe_get_workspace_layout(m.make_shape(4, H, 8, 2, 64, 1, "bf16"))
+    assert L["total"] - L["y"] >= 4 * 2 * (H * 2 + nb)
+
+
 def test_shared_workspace_layout(m):
     s = m.make_shape(4096, 4096, 64, 8, 1536, 1, "bf16")
     base = m.moe_workspace_size(s)
@@ -216,7 +239,7 @@ def test_shared_workspace_layout(m):
 
 @pytest.mark.parametrize("Is,code", [
     (0, "MOE_ERR_INVALID_ARG"), (-128, "MOE_ERR_INVALID_ARG"),
-    (96, "MOE_ERR_UNSUPPORTED"), (1 << 20, "MOE_ERR_UNSUPPORTED"),
+    (48, "MOE_ERR_UNSUPPORTED"), (1 << 20, "MOE_ERR_UNSUPPORTED"),
 ])
 def test_shared_width_validation(m, Is, code):
     s = m.make_shape(64, 4096, 8, 2, 128, 1, "bf16")

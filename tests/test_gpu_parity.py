@@ -125,6 +125,18 @@ SMALL = [
          sigma_g=0.02, sigma_w=0.02),
     dict(name="im384_three_col_tiles", T=257, H=768, E=10, k=3, Im=384, micro=1, dtype=mi.BF16,
          seed=19, sigma_g=0.02, sigma_w=0.02),
+    # shapes of the envelope's narrow end (H % 64, Im % 32): w13 tiles of 32
+    # gate + 32 up columns, down k-steps of 32 (a micro boundary at 160), a
+    # partial last down tile (H % 256 != 0) and its partial y block, router
+    # parts of unequal width (one of a single 32-wide chunk and several empty)
+    dict(name="h320_im96", T=300, H=320, E=8, k=2, Im=96, micro=1, dtype=mi.BF16, seed=20,
+         sigma_g=0.02, sigma_w=0.02),
+    dict(name="h448_im160_two_micro", T=200, H=448, E=6, k=3, Im=160, micro=2, dtype=mi.BF16, seed=21,
+         sigma_g=0.02, sigma_w=0.02),
+    dict(name="h384_im192_two_micro", T=250, H=384, E=8, k=2, Im=192, micro=2, dtype=mi.BF16, seed=22,
+         sigma_g=0.02, sigma_w=0.02),
+    dict(name="h64_im32", T=100, H=64, E=4, k=2, Im=32, micro=1, dtype=mi.BF16, seed=23),
+    dict(name="f32_h320_im96", T=150, H=320, E=8, k=2, Im=96, micro=2, dtype=mi.F32, seed=24),
     # every token on all 64 experts (the largest k)
     dict(name="all_experts_every_token", T=300, H=256, E=64, k=64, Im=128, micro=1, dtype=mi.BF16,
          seed=20, sigma_g=0.02, sigma_w=0.02),
@@ -598,6 +610,11 @@ SHARED = [
          sigma_g=0.02, sigma_w=0.02, Is=128),
     dict(name="bf16_wide_shared", T=300, H=256, E=6, k=2, Im=128, micro=1, dtype=mi.BF16, seed=44,
          sigma_g=0.02, sigma_w=0.02, Is=640),
+    # a routed width on the wide tiles beside a shared width that needs the
+    # narrow ones (the merged launches take the narrow shapes), H % 256 != 0
+    dict(name="h320_narrow_shared", T=300, H=320, E=8, k=2, Im=128, micro=1, dtype=mi.BF16, seed=45,
+         sigma_g=0.02, sigma_w=0.02, Is=96),
+    dict(name="f32_h448_shared", T=100, H=448, E=6, k=2, Im=160, micro=1, dtype=mi.F32, seed=46, Is=96),
 ]
 
 
