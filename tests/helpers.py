@@ -114,3 +114,38 @@ def assert_close_scaled(got, ref, dtype: str, what: str):
     assert not bad.any(), f"{what}: {int(bad.sum())} elements off, worst {float((d - bound).max()):.3e}"
     _, rl = errors(got, ref)
     assert rl <= tol_rel, f"{what}: rel-L2 {rl:.3e}"
+
+
+def random_shapes(n=24, seed=2024):
+    """Seeded layer shapes spread over the supported envelope (H % 64,
+    Im % 32, 1-3 micros, 1-64 experts, k <= 8, fp32 and bf16, some with a
+    shared expert of width Is % 32, skewed routing or no renormalisation),
+    plus small-token bf16 shapes that take the decode path.  Sizes stay
+    small enough for the oracle to run each in about a second."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = mi.F32 if rng.random() < 0.25 else mi.BF16
+        E = int(rng.integers(1, 65))
+        c = dict(T=int(rng.integers(1, 400)), H=64 * int(rng.integers(1, 9)), E=E,
+                 k=int(rng.integers(1, min(E, 8) + 1)), Im=32 * int(rng.integers(1, 9)),
+                 micro=int(rng.integers(1, 4)), dtype=dt, seed=300 + i, sigma_g=0.02, sigma_w=0.02,
+                 renormalize=bool(rng.random() < 0.85))
+        if rng.random() < 0.25:
+            c["zipf"] = {"s": 1.2, "scale": 6.0, "seed": 300 + i}
+        if rng.random() < 0.3:
+            c["Is"] = 32 * int(rng.integers(1, 9))
+        c["name"] = (f"r{i:02d}_T{c['T']}_H{c['H']}_E{E}_k{c['k']}_I{c['Im']}x{c['micro']}_{dt}"
+                     + (f"_Is{c['Is']}" if "Is" in c else ""))
+        out.append(c)
+    for i in range(4):  # the decode path: T <= 16, bf16, H % 2048, Im % 256
+        E = int(rng.integers(8, 65))
+        c = dict(T=int(rng.integers(1, 17)), H=2048, E=E, k=int(rng.integers(1, min(E, 8) + 1)),
+                 Im=256 * int(rng.integers(1, 3)), micro=int(rng.integers(1, 3)), dtype=mi.BF16,
+                 seed=400 + i, sigma_g=0.02, sigma_w=0.02, renormalize=True)
+        if i % 2:
+            c["Is"] = 256 * int(rng.integers(1, 3))
+        c["name"] = (f"d{i}_T{c['T']}_E{E}_k{c['k']}_I{c['Im']}x{c['micro']}"
+                     + (f"_Is{c['Is']}" if "Is" in c else ""))
+        out.append(c)
+    return out
