@@ -55,9 +55,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // wait-count tracking does not serialise the pipeline: callers wait on vmcnt
 // and barrier themselves before reading the destination.  lds and sbase must
 // be wave-uniform (scalar registers).
+// m0 is a reserved register (the compiler sets it right before each of its
+// own uses and keeps no value in it), so naming it as clobbered only states
+// what the asm does; clang warns that the clobber of a reserved register is
+// informational, which is silenced for this one statement.
 __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 // A pointer the caller knows to be wave-uniform, moved to scalar registers
