@@ -138,6 +138,14 @@ def random_shapes(n=24, seed=2024):
         c["name"] = (f"r{i:02d}_T{c['T']}_H{c['H']}_E{E}_k{c['k']}_I{c['Im']}x{c['micro']}_{dt}"
                      + (f"_Is{c['Is']}" if "Is" in c else ""))
         out.append(c)
+    # degenerate bf16 shapes: one expert, one token, every expert for every token
+    for j, c in enumerate([dict(T=77, H=320, E=1, k=1, Im=96, micro=2),
+                           dict(T=1, H=64, E=2, k=2, Im=32, micro=1),
+                           dict(T=130, H=256, E=8, k=8, Im=160, micro=1, Is=32)]):
+        c.update(dtype=mi.BF16, seed=380 + j, sigma_g=0.02, sigma_w=0.02, renormalize=True)
+        c["name"] = (f"e{j}_T{c['T']}_H{c['H']}_E{c['E']}_k{c['k']}_I{c['Im']}x{c['micro']}_bf16"
+                     + (f"_Is{c['Is']}" if "Is" in c else ""))
+        out.append(c)
     for i in range(4):  # the decode path: T <= 16, bf16, H % 2048, Im % 256
         E = int(rng.integers(8, 65))
         c = dict(T=int(rng.integers(1, 17)), H=2048, E=E, k=int(rng.integers(1, min(E, 8) + 1)),
