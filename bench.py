@@ -534,6 +534,7 @@ def time_decode(moe, torch, steps, warmup):
     rate = lambda ms: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
     ms_sh, Is, _, sh_bytes = time_shared(moe, torch, d3, steps, warmup, cold=True)
     sh_rate = (nbytes + sh_bytes) / (ms_sh * 1e-3) / 1e9
+    stack = time_decode_stack(moe, torch, steps, warmup)
     return {"ms": round(ms3, 5), "GB_per_s": round(rate(ms3), 1),
             "frac_of_hbm_peak": round(rate(ms3) / PEAK_HBM_GBS, 4), "active_experts": n_active,
             "algorithmic_bytes": nbytes, "cache": "evicted before every call", "per_call_ms": call_stats(ts),
@@ -545,7 +546,54 @@ def time_decode(moe, torch, steps, warmup):
                            "frac_of_hbm_peak": round(rate(ms_warm) / PEAK_HBM_GBS, 4)},
             "with_shared_expert": {"ms": round(ms_sh, 5), "shared_Im": Is, "shared_weight_bytes": sh_bytes,
                                    "GB_per_s": round(sh_rate, 1), "frac_of_hbm_peak": round(sh_rate / PEAK_HBM_GBS, 4),
-                                   "added_ms": round(ms_sh - ms3, 5), "cache": "evicted before every call"}}
+                                   "added_ms": round(ms_sh - ms3, 5), "cache": "evicted before every call"},
+            "layer_stack": stack}
+
+
+DECODE_STACK_LAYERS = 4
+
+
+def time_decode_stack(moe, torch, steps, warmup, n_layers=DECODE_STACK_LAYERS):
+    """Context for the decode figure: a decode step runs the MoE layers of a
+    model one after another, each with its own weights.  n_layers distinct
+    decode layers (the decode shape; weights and router drawn on the device
+    from a seeded generator, N(0, 0.02), since only time is measured here)
+    are called back to back on one stream, without an eviction between them
+    (their 4 x ~0.8 GB of active weights exceed the 256 MB infinity cache, so
+    every layer streams its own from HBM); the time per layer is the loop's
+    time over layers x steps."""
+    sp = mi.spec("decode")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261202)
+    bf = torch.bfloat16
+    shape = moe.make_shape(sp.T, sp.H, sp.E, sp.k, sp.Im, sp.micro, sp.dtype)
+    x = torch.randn(sp.T, sp.H, generator=gen, device="cuda").to(bf)
+    layers = []
+    for _ in range(n_layers):
+        wg = torch.randn(sp.E, sp.H, generator=gen, device="cuda") * 0.02
+        w1 = (torch.randn(sp.micro, sp.E, 2 * sp.Im, sp.H, generator=gen, device="cuda") * 0.02).to(bf)
+        w2 = (torch.randn(sp.micro, sp.E, sp.H, sp.Im, generator=gen, device="cuda") * 0.02).to(bf)
+        layers.append((wg, w1, w2, moe.MoELayerBuffers(shape)))
+    call = lambda: [b.forward(x, wg, None, w1, w2) for wg, w1, w2, b in layers]  # noqa: E731
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    settle(call, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (steps * n_layers)
+    actives = [int((b.views()["counts"].cpu().numpy() > 0).sum()) for _, _, _, b in layers]
+    nbytes = float(np.mean([decode_bytes(sp, a) for a in actives]))
+    rate = nbytes / (ms * 1e-3) / 1e9
+    del layers
+    return {"layers": n_layers, "ms_per_layer": round(ms, 5), "active_experts": actives,
+            "GB_per_s": round(rate, 1), "frac_of_hbm_peak": round(rate / PEAK_HBM_GBS, 4),
+            "note": "context: distinct decode layers back to back on one stream (weights drawn on the device), "
+                    "time per layer; the headline decode figure is one call with the cache evicted before it"}
 
 
 def time_only_layer(moe, torch, name, steps, warmup):
