@@ -53,15 +53,16 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 // (v_mfma_f64_16x16x4_f64, exact products, fp64 sums).  Sixteen waves, four
 // per SIMD (one wave alone cannot keep the matrix pipe busy, and four hide the
 // activation loads from HBM better than two): wave w covers the hidden part
-// hw = w % 8 -- the 32-wide chunks [hw*nc/8, (hw+1)*nc/8) of the nc = H/32
-// chunks, an eighth of H when H % 256 == 0 -- for the 16-expert tiles
-// q = 2*(w/8) and 2*(w/8)+1; lane (t = lane%16, g = lane/16) holds x[t][h0 + 8g + m] and
-// wg[16q + t][h0 + 8g + m] as the m-th MFMA's A and B elements, so the 8
-// MFMAs of a 32-wide chunk sum every h of the chunk exactly once.  The eight
-// partials are added in a fixed order, so the logits are reproducible run to
-// run.
+// w -- the 32-wide chunks [w*nc/16, (w+1)*nc/16) of the nc = H/32 chunks, a
+// sixteenth of H when H % 512 == 0 -- for all four 16-expert tiles q, so each
+// activation is loaded and converted once per workgroup (with a quarter of the
+// experts per wave it was loaded twice: 2-3 % slower); lane (t = lane%16,
+// g = lane/16) holds x[t][h0 + 8g + m] and wg[16q + t][h0 + 8g + m] as the
+// m-th MFMA's A and B elements, so the 8 MFMAs of a 32-wide chunk and tile sum
+// every h of the chunk exactly once.  The sixteen partials are added in a
+// fixed order, so the logits are reproducible run to run.
 constexpr int kRouteWaves = 16;
-constexpr int kHParts = kRouteWaves / 2;  // hidden parts (each wave: one part, one expert half)
+constexpr int kHParts = kRouteWaves;  // hidden parts (each wave: one part, all 64 experts)
 
 template <typename XT>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __restrict__ x,
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int hw = wave % kHParts, eh = wave / kHParts;  // hidden part, expert half
+  const int hw = wave;  // hidden part
   const int t0 = blockIdx.x * kTokTile;
   const int tl = lane & 15, g = lane >> 4;
   const int nc = H / 32;  // 32-wide chunks of the hidden dimension
@@ -89,57 +90,39 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(const XT* __res
   // rows past T and experts past E read the last valid row instead: their
   // logits are computed but never stored or ranked, so no operand is masked
   const XT* xrow = x + (size_t)min(t0 + tl, T - 1) * H + hb + 8 * g;
-  const float* wrow[2];
+  const float* wrow[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = 16 * (2 * eh + q) + tl;
+  for (int q = 0; q < 4; ++q) {
+    const int e = 16 * q + tl;
     wrow[q] = wg + (size_t)min(e, E - 1) * H + hb + 8 * g;
   }
 
-  f64x4 acc[2];
+  f64x4 acc[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // chunk loads are double-buffered: chunk c+32 is in flight while the
-  // 16 MFMAs of chunk c run (hq is a multiple of 32; the first chunk's load,
-  // issued before the loop, stays inside the row even when hq == 0, since
-  // cb < nc)
-  float xv[2][8], wv[2][2][8];
-  auto load_chunk = [&](int c, int b) {
-    load8(xrow + c, xv[b]);
+  // one chunk in registers at a time (hq is a multiple of 32, possibly 0):
+  // four waves per SIMD overlap one wave's loads with the others' MFMAs (a
+  // second chunk in flight per wave would spill at four expert tiles)
+  float xv[8], wv[4][8];
+  for (int c = 0; c < hq; c += 32) {
+    load8(xrow + c, xv);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) load8(wrow[q] + c, wv[b][q]);
-  };
-  auto mma_chunk = [&](int b) {
+    for (int q = 0; q < 4; ++q) load8(wrow[q] + c, wv[q]);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const double a = (double)xv[b][m];
+      const double a = (double)xv[m];
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)wv[b][q][m], acc[q], 0, 0, 0);
+      for (int q = 0; q < 4; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)wv[q][m], acc[q], 0, 0, 0);
     }
-  };
-  // the scheduling barriers keep each prefetch ahead of the MFMAs it is
-  // meant to overlap (left alone, the compiler sinks the loads to their use)
-  load_chunk(0, 0);
-  int c = 0;
-  for (; c + 64 <= hq; c += 64) {
-    load_chunk(c + 32, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_chunk(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (c + 64 < hq) load_chunk(c + 64, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_chunk(1);
-    __builtin_amdgcn_sched_barrier(0);
   }
-  if (c < hq) mma_chunk(0);  // trailing chunk (hq % 64 == 32), loaded above
   // fp64 16x16 D layout: register r of lane holds row (lane/16) + 4r (token),
   // column lane%16 (expert)
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[hw][g + 4 * r][16 * (2 * eh + q) + tl] = acc[q][r];
+    for (int r = 0; r < 4; ++r) part[hw][g + 4 * r][16 * q + tl] = acc[q][r];
   __syncthreads();
 
 #pragma unroll
