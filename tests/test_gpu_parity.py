@@ -6,6 +6,7 @@ the workload's tolerances.  Small layers are compared element by element;
 the full-size layers on every routing field, on every output element against
 the oracle's whole layer, and again on sampled output rows, which the oracle
 evaluates token by token."""
+import os
 import sys
 
 import numpy as np
@@ -803,7 +804,11 @@ def test_graph_replay_matches_eager(m, name, shared):
     del g
 
 
-RANDOM = random_shapes()
+# MOE_PARITY_SWEEP_SEEDS="1,2,3,4" adds random_shapes(25, seed) for each listed seed
+RANDOM = random_shapes() + [
+    dict(c, name=f"s{seed}_{c['name']}")
+    for seed in (int(v) for v in os.environ.get("MOE_PARITY_SWEEP_SEEDS", "").split(",") if v.strip())
+    for c in random_shapes(n=25, seed=seed)]
 
 
 @pytest.mark.parametrize("case", RANDOM, ids=[c["name"] for c in RANDOM])
