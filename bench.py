@@ -561,7 +561,9 @@ def time_decode_stack(moe, torch, steps, warmup, n_layers=DECODE_STACK_LAYERS):
     are called back to back on one stream, without an eviction between them
     (their 4 x ~0.8 GB of active weights exceed the 256 MB infinity cache, so
     every layer streams its own from HBM); the time per layer is the loop's
-    time over layers x steps."""
+    time over layers x steps.  The same calls are also captured as one HIP
+    graph and replayed back to back (graph: time per layer, and whether every
+    layer's output equals the eager one bit for bit)."""
     sp = mi.spec("decode")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261202)
@@ -586,12 +588,38 @@ def time_decode_stack(moe, torch, steps, warmup, n_layers=DECODE_STACK_LAYERS):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (steps * n_layers)
+    eager_out = [b.out.clone() for _, _, _, b in layers]
+    # the same n_layers calls captured as one HIP graph and replayed back to back
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    settle(g.replay, torch)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / (steps * n_layers)
+    same = all(torch.equal(b.out.view(torch.int16), o.view(torch.int16)) for (_, _, _, b), o in zip(layers, eager_out))
+    del g
     actives = [int((b.views()["counts"].cpu().numpy() > 0).sum()) for _, _, _, b in layers]
     nbytes = float(np.mean([decode_bytes(sp, a) for a in actives]))
     rate = nbytes / (ms * 1e-3) / 1e9
     del layers
+    rate_g = nbytes / (ms_graph * 1e-3) / 1e9
     return {"layers": n_layers, "ms_per_layer": round(ms, 5), "active_experts": actives,
             "GB_per_s": round(rate, 1), "frac_of_hbm_peak": round(rate / PEAK_HBM_GBS, 4),
+            "graph": {"ms_per_layer": round(ms_graph, 5), "GB_per_s": round(rate_g, 1),
+                      "frac_of_hbm_peak": round(rate_g / PEAK_HBM_GBS, 4), "output_equals_eager": same},
             "note": "context: distinct decode layers back to back on one stream (weights drawn on the device), "
                     "time per layer; the headline decode figure is one call with the cache evicted before it"}
 
